@@ -1,0 +1,529 @@
+"""Independent checks that pin the oracle (and, through it, the library).
+
+Nothing here calls the oracle's arithmetic: each check recomputes what the
+definitions fix by another route -- exact rational arithmetic, a classic
+breadth-first DBSCAN, scipy / scikit-learn routines, closed forms on
+lattices and invariants -- and compares.  Every ``check_*`` function takes
+a loaded oracle (``oracle.Oracle``) and raises AssertionError on a
+mismatch, so the same suite can also be run against deliberately broken
+copies of the oracle to show that it catches them.
+
+Definitions followed (Wang et al., "Design and optimization of DBSCAN
+Algorithm based on CUDA", Sec. II items 1-3 and the cluster definition;
+Sec. IV-A for comparing with eps^2).
+"""
+from __future__ import annotations
+
+import json
+import os
+from collections import deque
+from fractions import Fraction
+
+import numpy as np
+
+from all_pairs_distance_amd import datagen
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+U32 = Fraction(1, 2 ** 24)          # unit roundoff of binary32
+
+
+# ------------------------------------------------------ exact binary32 model
+
+def rn32(q: Fraction) -> Fraction:
+    """Round a rational to the nearest binary32 value, ties to even, with
+    gradual underflow (no overflow handling: inputs stay far below 2^128)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = -q if q < 0 else q
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                 # below 2^-126 the spacing stays 2^-149
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    whole = m.numerator // m.denominator
+    rest = m - whole
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and whole % 2 == 1):
+        whole += 1
+    return sign * whole * ulp
+
+
+def exact_d2_rounded(a, b) -> np.float32:
+    """The fixed fp32 distance evaluated in exact rational arithmetic with an
+    explicit rounding after each operation (dimensions ascending)."""
+    s = Fraction(0)
+    for x, y in zip(np.asarray(a, np.float32).ravel(),
+                    np.asarray(b, np.float32).ravel()):
+        t = rn32(Fraction(float(x)) - Fraction(float(y)))
+        q = rn32(t * t)
+        s = rn32(s + q)
+    return np.float32(float(s))
+
+
+def exact_d2_real(a, b) -> Fraction:
+    """The true squared distance of the two binary32 vectors (no rounding)."""
+    s = Fraction(0)
+    for x, y in zip(np.asarray(a, np.float32).ravel(),
+                    np.asarray(b, np.float32).ravel()):
+        t = Fraction(float(x)) - Fraction(float(y))
+        s += t * t
+    return s
+
+
+def eps2_of(eps) -> np.float32:
+    e = np.float32(eps)
+    return np.float32(float(rn32(Fraction(float(e)) * Fraction(float(e)))))
+
+
+# --------------------------------------------------- float32 step emulation
+
+def d2_to_all(x: np.ndarray, i: int) -> np.ndarray:
+    """Squared distance from point i to every point, numpy float32, one
+    dimension at a time in ascending order (no reduction reordering)."""
+    s = np.zeros(x.shape[0], dtype=np.float32)
+    for k in range(x.shape[1]):
+        t = x[:, k] - x[i, k]
+        s = s + t * t
+    return s
+
+
+def neighbour_lists(x: np.ndarray, eps) -> list[np.ndarray]:
+    e2 = eps2_of(eps)
+    return [np.nonzero(d2_to_all(x, i) <= e2)[0] for i in range(x.shape[0])]
+
+
+# ----------------------------------------------------- classic DBSCAN (BFS)
+
+def bfs_dbscan(x: np.ndarray, eps, min_pts: int):
+    """Ester et al.'s expansion: visit points in index order, grow a cluster
+    from each unvisited core point by breadth-first search over
+    neighbourhoods, expanding only through core points.  Returns
+    (cluster id per point or -1, core mask, neighbour lists)."""
+    nb = neighbour_lists(x, eps)
+    n = x.shape[0]
+    core = np.array([len(v) >= min_pts for v in nb], dtype=bool)
+    unvisited, noise = -2, -1
+    lab = np.full(n, unvisited, dtype=np.int64)
+    cid = 0
+    for p in range(n):
+        if lab[p] != unvisited:
+            continue
+        if not core[p]:
+            lab[p] = noise
+            continue
+        lab[p] = cid
+        queue = deque(nb[p])
+        while queue:
+            q = queue.popleft()
+            if lab[q] == noise:
+                lab[q] = cid
+            if lab[q] != unvisited:
+                continue
+            lab[q] = cid
+            if core[q]:
+                queue.extend(nb[q])
+        cid += 1
+    return lab, core, nb
+
+
+def canonical_from_partition(cluster_of_core: np.ndarray, core: np.ndarray,
+                             nb: list[np.ndarray]) -> np.ndarray:
+    """Apply the border and label rules to a core partition: a non-core point
+    joins the cluster of its lowest-index core neighbour; every cluster is
+    labelled by its smallest member; the rest is noise (-1)."""
+    n = core.size
+    cl = np.full(n, -1, dtype=np.int64)
+    cl[core] = cluster_of_core[core]
+    for p in np.nonzero(~core)[0]:
+        cn = [c for c in nb[p] if core[c]]
+        if cn:
+            cl[p] = cluster_of_core[min(cn)]
+    labels = np.full(n, -1, dtype=np.int32)
+    smallest = {}
+    for i in range(n):
+        if cl[i] >= 0 and cl[i] not in smallest:
+            smallest[cl[i]] = i
+    for i in range(n):
+        if cl[i] >= 0:
+            labels[i] = smallest[cl[i]]
+    return labels
+
+
+def bfs_canonical(x, eps, min_pts):
+    lab, core, nb = bfs_dbscan(x, eps, min_pts)
+    counts = np.array([len(v) for v in nb], dtype=np.int32)
+    return canonical_from_partition(lab, core, nb), counts
+
+
+# --------------------------------------------------------------- invariants
+
+def check_label_invariants(x, eps, min_pts, labels, counts):
+    """Properties every correct result has, whatever the input."""
+    n = x.shape[0]
+    labels = np.asarray(labels)
+    counts = np.asarray(counts)
+    assert labels.shape == (n,) and counts.shape == (n,)
+    assert np.all(counts >= 1) and np.all(counts <= n)
+    assert (int(counts.astype(np.int64).sum()) - n) % 2 == 0
+    core = counts >= min_pts
+    nb = neighbour_lists(x, eps)
+    assert np.array_equal(counts, [len(v) for v in nb])
+    for i in range(n):
+        cn = [c for c in nb[i] if core[c]]
+        if labels[i] == -1:
+            assert not core[i] and not cn, f"noise point {i} has a core neighbour"
+            continue
+        assert 0 <= labels[i] <= i
+        assert labels[labels[i]] == labels[i]
+        if core[i]:
+            for c in cn:
+                assert labels[c] == labels[i], f"cores {i},{c} split"
+        else:
+            assert cn, f"border point {i} without core neighbour"
+            assert labels[i] == labels[min(cn)]
+
+
+# ------------------------------------------------------------------- checks
+
+def load_handworked():
+    with open(os.path.join(GOLDEN, "handworked.json")) as f:
+        cases = json.load(f)["cases"]
+    out = []
+    for c in cases:
+        if "lattice" in c:
+            pts = datagen.integer_lattice(c["lattice"]["side"], c["lattice"]["d"])
+        else:
+            pts = np.array(c["points"], dtype=np.float32)
+        out.append((c["id"], pts, c["eps"], c["min_pts"],
+                    np.array(c["counts"], np.int32),
+                    np.array(c["labels"], np.int32)))
+    return out
+
+
+def check_handworked(o):
+    for cid, pts, eps, m, counts, labels in load_handworked():
+        lab, cnt, _ = o.fit(pts, eps, m)
+        assert np.array_equal(cnt, counts), (cid, cnt, counts)
+        assert np.array_equal(lab, labels), (cid, lab, labels)
+
+
+def boundary_pairs():
+    """Pairs whose squared distance lands on or next to eps^2 in fp32."""
+    e = np.float32(0.03)
+    pairs = [(0.0, e)]
+    for base in (0.1, 0.2, 0.5, 0.7, 0.25, 1.0, 3.0, 100.0):
+        a = np.float32(base)
+        b = np.float32(np.float32(base) + e)
+        pairs.append((a, b))
+        for k in (-2, -1, 1, 2):
+            pairs.append((a, np.nextafter(b, np.float32(np.inf) if k > 0
+                                          else np.float32(-np.inf))))
+    return [(np.array([p], np.float32), np.array([q], np.float32)) for p, q in pairs]
+
+
+def random_pairs(rng, count=400):
+    out = []
+    for _ in range(count):
+        d = int(rng.choice([1, 2, 3, 4, 5, 8, 13, 17, 64]))
+        scale = float(rng.choice([1e-3, 1.0, 7.0, 1e3]))
+        a = (rng.standard_normal(d) * scale).astype(np.float32)
+        b = (a + rng.standard_normal(d) * scale * float(rng.choice([1e-4, 0.01, 1.0]))).astype(np.float32)
+        out.append((a, b))
+    return out
+
+
+def check_d2_exact(o, seed=7):
+    """Oracle d2 == exact-rational model, bit for bit, on boundary and random
+    pairs; and it lies within the forward error bound of the true value."""
+    rng = np.random.default_rng(seed)
+    for a, b in boundary_pairs() + random_pairs(rng):
+        got = o.d2(a, b)
+        want = exact_d2_rounded(a, b)
+        assert got.tobytes() == want.tobytes(), (a, b, got, want)
+        assert o.d2(b, a).tobytes() == got.tobytes()
+        real = exact_d2_real(a, b)
+        bound = ((1 + U32) ** (a.size + 2) - 1) * real
+        if real == 0 or real > Fraction(2) ** -100:
+            assert abs(Fraction(float(got)) - real) <= bound, (a, b)
+
+
+def check_d2_order_and_rounding(o):
+    """Cases where another summation order, a fused multiply-add or a flush
+    of subnormals would give different bits."""
+    # left-to-right: (1 + 2^-24) + 2^-24 rounds to 1 twice (ties to even);
+    # summing the two small terms first would give 1 + 2^-23.
+    h = np.float32(2.0 ** -12)
+    a = np.array([1.0, h, h], np.float32)
+    z = np.zeros(3, np.float32)
+    assert o.d2(a, z) == np.float32(1.0)
+    assert o.d2(a[::-1].copy(), z) == np.float32(1.0 + 2.0 ** -23)
+    # fused vs separate rounding of s + t*t
+    rng = np.random.default_rng(3)
+    hits = 0
+    for _ in range(4000):
+        a = rng.random(2).astype(np.float32)
+        b = rng.random(2).astype(np.float32)
+        got = o.d2(a, b)
+        assert got.tobytes() == exact_d2_rounded(a, b).tobytes()
+        t0 = Fraction(float(a[0])) - Fraction(float(b[0]))
+        t1 = rn32(Fraction(float(a[1])) - Fraction(float(b[1])))
+        fused = rn32(rn32(rn32(t0) ** 2) + t1 * t1)
+        hits += fused != Fraction(float(got))
+    assert hits > 0  # the sample does contain pairs where fusing changes bits
+    # gradual underflow: (1e-20)^2 = 1e-40 is subnormal in binary32
+    tiny = np.array([1e-20], np.float32)
+    zero = np.array([0.0], np.float32)
+    v = o.d2(tiny, zero)
+    assert v > 0 and v < np.finfo(np.float32).tiny
+    assert v.tobytes() == exact_d2_rounded(tiny, zero).tobytes()
+    lab, cnt, _ = o.fit(np.array([[0.0], [1e-20]], np.float32), 0.0, 1)
+    assert cnt.tolist() == [1, 1] and lab.tolist() == [0, 1]
+
+
+def check_eps2(o):
+    for eps in (0.03, 0.01, 0.05, 0.003, 0.35, 0.5, 1.0, 0.1, 1e-20, 0.0):
+        assert o.eps2(eps).tobytes() == eps2_of(eps).tobytes()
+    # the fp32 chain x_k = fl32(k * 0.03): consecutive gaps straddle eps
+    x = datagen.collinear_chain(12, 0.03)
+    e2 = eps2_of(0.03)
+    want = [bool(exact_d2_rounded(x[k], x[k + 1]) <= e2) for k in range(11)]
+    lab, cnt, _ = o.fit(x, 0.03, 1)
+    expect_cnt = np.ones(12, np.int32)
+    for k in range(11):
+        if want[k]:
+            expect_cnt[k] += 1
+            expect_cnt[k + 1] += 1
+    # non-consecutive points are >= 0.06 apart, far outside eps
+    assert np.array_equal(cnt, expect_cnt), (cnt, expect_cnt, want)
+    assert want != [True] * 11 and want != [False] * 11
+
+
+def small_cases(seed=11, count=60):
+    rng = np.random.default_rng(seed)
+    out = []
+    for t in range(count):
+        n = int(rng.integers(1, 160))
+        d = int(rng.choice([1, 2, 3, 5, 8]))
+        kind = t % 4
+        if kind == 0:
+            x = datagen.uniform_points(n, d, seed * 1000 + t)
+        elif kind == 1:
+            x = datagen.gaussian_blobs(n, d, seed * 1000 + t, n_blobs=3,
+                                       sigma=0.03, noise_frac=0.2)
+        elif kind == 2:   # integer coordinates: many exact ties at eps
+            x = rng.integers(0, 4, (n, d)).astype(np.float32)
+        else:             # duplicates
+            base = datagen.uniform_points(max(n // 3, 1), d, seed * 1000 + t)
+            x = np.ascontiguousarray(base[rng.integers(0, base.shape[0], n)])
+        if kind == 2:
+            eps = float(rng.choice([0.0, 1.0, 1.5, 2.0]))
+        else:
+            eps = float(rng.choice([0.0, 0.05, 0.1, 0.2, 0.35]))
+        m = int(rng.integers(1, 8))
+        out.append((x, eps, m))
+    return out
+
+
+def check_bfs(o, seed=11, count=60):
+    """Oracle == breadth-first DBSCAN after applying the canonical border and
+    label rules (the core partition is order-independent)."""
+    for x, eps, m in small_cases(seed, count):
+        lab, cnt, _ = o.fit(x, eps, m)
+        want_lab, want_cnt = bfs_canonical(x, eps, m)
+        assert np.array_equal(cnt, want_cnt), (x.shape, eps, m)
+        assert np.array_equal(lab, want_lab), (x.shape, eps, m)
+
+
+def check_invariants(o, seed=23, count=40):
+    for x, eps, m in small_cases(seed, count):
+        lab, cnt, _ = o.fit(x, eps, m)
+        check_label_invariants(x, eps, m, lab, cnt)
+
+
+def margin_clean(x: np.ndarray, eps: float, rel=1e-4) -> bool:
+    """True if no pair's true distance is within a relative band of eps, so
+    a float64 library routine and the fp32 formula must agree on it."""
+    x64 = x.astype(np.float64)
+    e = float(np.float32(eps))
+    for i in range(x.shape[0]):
+        dist = np.sqrt(((x64 - x64[i]) ** 2).sum(axis=1))
+        if np.any(np.abs(dist - e) <= rel * e):
+            return False
+    return True
+
+
+def clean_blob_cases(seed, count, n_range=(50, 400)):
+    rng = np.random.default_rng(seed)
+    out = []
+    t = 0
+    while len(out) < count:
+        t += 1
+        n = int(rng.integers(*n_range))
+        d = int(rng.choice([2, 3, 4, 8]))
+        x = datagen.gaussian_blobs(n, d, seed * 7919 + t, n_blobs=4,
+                                   sigma=0.04, noise_frac=0.15)
+        eps = float(rng.choice([0.04, 0.06, 0.1]))
+        if margin_clean(x, eps):
+            out.append((x, eps, int(rng.integers(2, 10))))
+    return out
+
+
+def check_sklearn(o, seed=5, count=12):
+    """Core set, noise set and core partition equal scikit-learn's DBSCAN
+    (float64, brute force) on inputs with no pair near the eps boundary;
+    scikit-learn's border choice is order-dependent, so a border point is
+    only required to sit in the cluster of one of its core neighbours."""
+    from sklearn.cluster import DBSCAN
+    for x, eps, m in clean_blob_cases(seed, count):
+        lab, cnt, _ = o.fit(x, eps, m)
+        sk = DBSCAN(eps=float(np.float32(eps)), min_samples=m,
+                    algorithm="brute").fit(x.astype(np.float64))
+        sk_core = np.zeros(x.shape[0], bool)
+        sk_core[sk.core_sample_indices_] = True
+        core = cnt >= m
+        assert np.array_equal(core, sk_core)
+        assert np.array_equal(lab == -1, sk.labels_ == -1)
+        ours, theirs = lab[core], sk.labels_[core]
+        # same partition of the cores: a bijection between label values
+        pairs = set(zip(ours.tolist(), theirs.tolist()))
+        assert len(pairs) == len(set(ours.tolist())) == len(set(theirs.tolist()))
+
+
+def check_kdtree_counts(o, seed=9, count=10):
+    """Neighbour counts equal scipy's k-d tree ball counts (float64, closed
+    ball) on inputs with no pair near the eps boundary."""
+    from scipy.spatial import cKDTree
+    for x, eps, m in clean_blob_cases(seed, count):
+        _, cnt, _ = o.fit(x, eps, m)
+        tree = cKDTree(x.astype(np.float64))
+        want = tree.query_ball_point(x.astype(np.float64),
+                                     r=float(np.float32(eps)),
+                                     return_length=True)
+        assert np.array_equal(cnt, want)
+
+
+def check_components(o, seed=13, count=10):
+    """MinPts = 1: every point is core and the clusters are the connected
+    components of the eps-graph (scipy), each labelled by its smallest
+    index."""
+    from scipy.sparse import csr_matrix
+    from scipy.sparse.csgraph import connected_components
+    for x, eps, _ in clean_blob_cases(seed, count):
+        lab, _, _ = o.fit(x, eps, 1)
+        x64 = x.astype(np.float64)
+        e = float(np.float32(eps))
+        n = x.shape[0]
+        rows, cols = [], []
+        for i in range(n):
+            dist = np.sqrt(((x64 - x64[i]) ** 2).sum(axis=1))
+            js = np.nonzero(dist <= e)[0]
+            rows.extend([i] * js.size)
+            cols.extend(js.tolist())
+        g = csr_matrix((np.ones(len(rows)), (rows, cols)), shape=(n, n))
+        _, comp = connected_components(g, directed=False)
+        smallest = {}
+        for i in range(n):
+            smallest.setdefault(comp[i], i)
+        want = np.array([smallest[comp[i]] for i in range(n)], np.int32)
+        assert np.array_equal(lab, want)
+
+
+def _sq32(t) -> np.float32:
+    t = np.float32(t)
+    return np.float32(t * t)
+
+
+def two_pointer_counts_1d(x: np.ndarray, eps) -> np.ndarray:
+    """d = 1: fl32(|a-b|)^2 grows with |a-b|, so each neighbourhood is a
+    window of the sorted values; slide both window ends."""
+    v = x.ravel()
+    order = np.argsort(v, kind="stable")
+    s = v[order]
+    e2 = eps2_of(eps)
+    n = s.size
+    lo = hi = 0
+    out = np.empty(n, np.int32)
+    for k in range(n):
+        while lo < k and _sq32(s[k] - s[lo]) > e2:
+            lo += 1
+        if hi < k:
+            hi = k
+        while hi + 1 < n and _sq32(s[hi + 1] - s[k]) <= e2:
+            hi += 1
+        out[order[k]] = hi - lo + 1
+    return out
+
+
+def check_closed_forms(o):
+    rng = np.random.default_rng(17)
+    # d = 1: sorted two-pointer windows
+    for t in range(12):
+        n = int(rng.integers(1, 400))
+        x = (rng.random(n) * rng.choice([1.0, 10.0])).astype(np.float32)
+        if t % 3 == 0:
+            x = np.round(x * 8) / np.float32(8)   # exact ties
+        eps = float(rng.choice([0.0, 0.01, 0.125, 0.5]))
+        _, cnt, _ = o.fit(x.reshape(-1, 1), eps, 1)
+        assert np.array_equal(cnt, two_pointer_counts_1d(x, eps))
+    # eps at least the diameter: one cluster labelled 0, all counts n
+    for d in (1, 2, 7):
+        x = datagen.uniform_points(97, d, 100 + d)
+        lab, cnt, _ = o.fit(x, 10.0, 5)
+        assert np.all(cnt == 97) and np.all(lab == 0)
+    # eps = 0: counts are the multiplicities of exact duplicates
+    base = datagen.uniform_points(20, 3, 5)
+    idx = rng.integers(0, 20, 150)
+    x = np.ascontiguousarray(base[idx])
+    lab, cnt, _ = o.fit(x, 0.0, 1)
+    mult = np.bincount(idx, minlength=20)[idx]
+    assert np.array_equal(cnt, mult)
+    first = {}
+    for i, k in enumerate(idx.tolist()):
+        first.setdefault(k, i)
+    assert np.array_equal(lab, [first[k] for k in idx.tolist()])
+    # lattices {0..m-1}^2, eps 1, MinPts 5: interior core, edges border,
+    # corners noise, label = index 1 (the point (1, 0))
+    for m in (3, 4, 9):
+        x = datagen.integer_lattice(m, 2)
+        lab, cnt, _ = o.fit(x, 1.0, 5)
+        corner = {0, m - 1, m * (m - 1), m * m - 1}
+        want = np.array([-1 if i in corner else 1 for i in range(m * m)], np.int32)
+        assert np.array_equal(lab, want)
+    # {0..m-1}^3, eps 1, MinPts 7: interior core (6 + self), face points
+    # border, edge and corner points noise; label = index 1 + m (1, 1, 0)
+    for m in (3, 5):
+        x = datagen.integer_lattice(m, 3)
+        lab, cnt, _ = o.fit(x, 1.0, 7)
+        want = []
+        for i in range(m ** 3):
+            c = (i % m, (i // m) % m, i // (m * m))
+            on_bound = sum(v in (0, m - 1) for v in c)
+            want.append(1 + m if on_bound <= 1 else -1)
+        assert np.array_equal(lab, np.array(want, np.int32))
+
+
+def check_argument_errors(o):
+    x = np.zeros((4, 2), np.float32)
+    assert o.fit_status(x, 4, 2, 0.1, 0) == -1        # min_pts < 1
+    assert o.fit_status(x, 4, 0, 0.1, 1) == -1        # d < 1
+    assert o.fit_status(x, -1, 2, 0.1, 1) == -1       # n < 0
+    assert o.fit_status(x, 4, 2, -0.1, 1) == -1       # eps < 0
+    assert o.fit_status(x, 4, 2, float("nan"), 1) == -1
+    assert o.fit_status(x, 4, 2, float("inf"), 1) == -1
+    assert o.fit_status(None, 4, 2, 0.1, 1) == -1
+    assert o.fit_status(None, 0, 2, 0.1, 1) == 0       # n = 0 is a no-op
+    bad = x.copy()
+    bad[2, 1] = np.nan
+    assert o.fit_status(bad, 4, 2, 0.1, 1) == -2
+    bad[2, 1] = np.inf
+    assert o.fit_status(bad, 4, 2, 0.1, 1) == -2
+
+
+ALL_CHECKS = [check_handworked, check_d2_exact, check_d2_order_and_rounding,
+              check_eps2, check_bfs, check_invariants, check_sklearn,
+              check_kdtree_counts, check_components, check_closed_forms,
+              check_argument_errors]

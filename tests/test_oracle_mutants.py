@@ -1,0 +1,88 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and show
+that the pin suite catches every one of them.
+
+Each mutant is oracle.c with one textual change (or one changed compiler
+flag), built into a temporary library; the real oracle is never modified.
+A mutant that passes every pin would mean the pins cannot tell that
+mistake from the definition.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import pins
+
+ORACLE_DIR = os.path.dirname(oracle.__file__)
+
+COUNT_LOOP = ("    for (int64_t j = 0; j < n; ++j)\n"
+              "      if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) ++c;\n"
+              "    count[i] = (int32_t)c;")
+
+MUTANTS = {
+    # comparison at the radius made strict
+    "strict_radius": [("<= eps2", "< eps2")],
+    # a point no longer counts itself
+    "self_excluded": [(COUNT_LOOP, COUNT_LOOP.replace(
+        "if (oracle_d2", "if (j != i && oracle_d2"))],
+    # core test made strict
+    "core_strict": [("count[i] >= min_pts", "count[i] > min_pts")],
+    # radius not squared
+    "eps_not_squared": [("float e2 = eps * eps;", "float e2 = eps;")],
+    # last dimension dropped from the distance
+    "dropped_dim": [("for (int32_t k = 0; k < d; ++k) {",
+                     "for (int32_t k = 0; k + 1 < d; ++k) {")],
+    # sign error in the difference
+    "wrong_sign": [("float t = a[k] - b[k];", "float t = a[k] + b[k];")],
+    # dimensions summed in reverse order
+    "reversed_sum": [("for (int32_t k = 0; k < d; ++k) {",
+                      "for (int32_t k = d - 1; k >= 0; --k) {")],
+    # row stride forgotten (transposed operand indexing)
+    "bad_stride": [(COUNT_LOOP, COUNT_LOOP.replace("p + j * (int64_t)d", "p + j"))],
+    # clusters merged through non-core points
+    "merge_through_border": [("          if (!core[j]) continue;\n", "")],
+    # border point takes its highest-index core neighbour
+    "border_last_core": [("        bmin[i] = (int32_t)c;\n        break;\n",
+                          "        bmin[i] = (int32_t)c;\n")],
+    # label is the union-find root (smallest core) instead of the smallest member
+    "label_is_root": [("labels[i] = first[r];", "labels[i] = r;")],
+    # noise labelled 0 instead of -1
+    "noise_zero": [("else { labels[i] = -1; continue; }",
+                    "else { labels[i] = 0; continue; }")],
+    # border points treated as noise
+    "no_borders": [("else if (bmin[i] >= 0) r = uf_find(parent, bmin[i]);",
+                    "else if (0) r = 0;")],
+}
+
+FLAG_MUTANTS = {
+    # s + t*t fused into one rounding
+    "fused_multiply_add": ["-ffp-contract=fast", "-mfma"],
+}
+
+
+def build_mutant(tmp_path, name):
+    shutil.copy(os.path.join(ORACLE_DIR, "oracle.h"), tmp_path / "oracle.h")
+    with open(os.path.join(ORACLE_DIR, "oracle.c")) as f:
+        src = f.read()
+    for old, new in MUTANTS.get(name, []):
+        assert src.count(old) >= 1, (name, old)
+        src = src.replace(old, new)
+    path = tmp_path / "oracle.c"
+    path.write_text(src)
+    lib = oracle.build(force=True, src=str(path), out=str(tmp_path / "lib.so"),
+                       extra=FLAG_MUTANTS.get(name))
+    return oracle.Oracle(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(FLAG_MUTANTS))
+def test_pins_catch_mutant(tmp_path, name):
+    o = build_mutant(tmp_path, name)
+    caught = None
+    for check in pins.ALL_CHECKS:
+        try:
+            check(o)
+        except Exception as exc:  # AssertionError, or an error status
+            caught = (check.__name__, type(exc).__name__)
+            break
+    assert caught is not None, f"mutant {name} passed every pin"
