@@ -1,0 +1,337 @@
+// C ABI of the DBSCAN library: argument checks, workspace carving and the
+// launch sequence of one fit.  See include/dbscan.h for the contract.
+#include <climits>
+#include <cmath>
+#include <cstring>
+
+#include "dbscan.h"
+#include "internal.h"
+
+namespace dbk {
+
+int pick_dim(int d) {
+  for (int D : kDims)
+    if (D >= d) return D;
+  return 0;
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static int64_t pad_points(int64_t n) {
+  return (n + kPadPoints - 1) / kPadPoints * kPadPoints;
+}
+
+// Region sizes in carve order; every region starts 256-byte aligned.
+static size_t regions(int64_t n_pad, int S, size_t* out) {
+  const size_t np = (size_t)n_pad;
+  size_t sz[] = {
+      sizeof(Status),                // status
+      np * S * sizeof(float),        // pts
+      np * sizeof(unsigned),         // count
+      np,                            // core
+      np * sizeof(int),              // parent
+      np * sizeof(int),              // bmin
+      np * sizeof(int),              // cmin
+      np * sizeof(int),              // core_list
+      np * S * sizeof(float),        // core_pts
+      (np / 1024 + 1) * sizeof(unsigned),  // block_sums
+  };
+  size_t total = 0;
+  for (int r = 0; r < 10; ++r) {
+    if (out) out[r] = total;
+    total += align_up(sz[r], 256);
+  }
+  return total;
+}
+
+size_t layout_min_bytes(int64_t n, int d) {
+  const int D = pick_dim(d);
+  if (n < 0 || n > INT32_MAX || D == 0) return 0;
+  return regions(pad_points(n < 1 ? 1 : n), row_stride(D), nullptr);
+}
+
+bool carve(Layout& L, void* ws, size_t ws_bytes) {
+  size_t off[10];
+  const size_t need = regions(L.n_pad, L.stride, off);
+  if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 255u)) return false;
+  char* b = static_cast<char*>(ws);
+  L.status = reinterpret_cast<Status*>(b + off[0]);
+  L.pts = reinterpret_cast<float*>(b + off[1]);
+  L.count = reinterpret_cast<unsigned*>(b + off[2]);
+  L.core = reinterpret_cast<unsigned char*>(b + off[3]);
+  L.parent = reinterpret_cast<int*>(b + off[4]);
+  L.bmin = reinterpret_cast<int*>(b + off[5]);
+  L.cmin = reinterpret_cast<int*>(b + off[6]);
+  L.core_list = reinterpret_cast<int*>(b + off[7]);
+  L.core_pts = reinterpret_cast<float*>(b + off[8]);
+  L.block_sums = reinterpret_cast<unsigned*>(b + off[9]);
+  L.bytes_min = need;
+  const size_t spare = ws_bytes - need;
+  L.edges = reinterpret_cast<uint2*>(b + need);
+  L.edge_cap = spare / sizeof(uint2);
+  if (L.edge_cap == 0) L.edges = nullptr;
+  return true;
+}
+
+}  // namespace dbk
+
+using namespace dbk;
+
+namespace {
+
+constexpr uint32_t kKnownFlags =
+    DBSCAN_FLAG_TIME_PHASES | DBSCAN_FLAG_FORCE_TILE_MERGE;
+
+int check_args(int64_t n, int32_t d, float eps, int32_t min_pts) {
+  if (n < 0 || n > (int64_t)INT32_MAX) return DBSCAN_ERR_INVALID_ARG;
+  if (d < 1 || d > DBSCAN_MAX_D) return DBSCAN_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || std::isinf(eps)) return DBSCAN_ERR_INVALID_ARG;
+  if (min_pts < 1) return DBSCAN_ERR_INVALID_ARG;
+  return DBSCAN_OK;
+}
+
+int map_hip(hipError_t e) {
+  if (e == hipSuccess) return DBSCAN_OK;
+  if (e == hipErrorNoDevice || e == hipErrorNoBinaryForGpu ||
+      e == hipErrorInvalidDeviceFunction || e == hipErrorInsufficientDriver)
+    return DBSCAN_ERR_NO_DEVICE;
+  if (e == hipErrorOutOfMemory) return DBSCAN_ERR_OOM;
+  return DBSCAN_ERR_HIP;
+}
+
+int have_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+    (void)hipGetLastError();
+    return DBSCAN_ERR_NO_DEVICE;
+  }
+  return DBSCAN_OK;
+}
+
+// Phase timing with HIP events on the fit's stream.
+struct PhaseTimer {
+  bool on = false;
+  hipEvent_t ev[6] = {};
+  hipStream_t s = nullptr;
+  explicit PhaseTimer(bool enable, hipStream_t stream) : s(stream) {
+    if (!enable) return;
+    on = true;
+    for (auto& e : ev)
+      if (hipEventCreate(&e) != hipSuccess) on = false;
+  }
+  void mark(int k) {
+    if (on) (void)hipEventRecord(ev[k], s);
+  }
+  float ms(int a, int b) {
+    float t = 0.f;
+    if (on && hipEventElapsedTime(&t, ev[a], ev[b]) != hipSuccess) t = -1.f;
+    return t;
+  }
+  ~PhaseTimer() {
+    for (auto& e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
+
+#define DB_TRY(expr)                      \
+  do {                                    \
+    hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) {               \
+      (void)hipStreamSynchronize(stream); \
+      if (info) info->hip_error = (int32_t)e_; \
+      return map_hip(e_);                 \
+    }                                     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t dbscan_workspace_bytes(int64_t n, int32_t d) {
+  if (d < 1 || d > DBSCAN_MAX_D) return 0;
+  return layout_min_bytes(n, d);
+}
+
+size_t dbscan_workspace_bytes_with_edges(int64_t n, int32_t d,
+                                         int64_t max_edges) {
+  const size_t base = dbscan_workspace_bytes(n, d);
+  if (base == 0 || max_edges < 0) return 0;
+  return align_up(base + (size_t)max_edges * sizeof(uint2), 256);
+}
+
+int dbscan_abi_version(void) { return DBSCAN_ABI_VERSION; }
+
+const char* dbscan_status_string(int status) {
+  switch (status) {
+    case DBSCAN_OK: return "ok";
+    case DBSCAN_ERR_INVALID_ARG: return "invalid argument";
+    case DBSCAN_ERR_NONFINITE: return "a coordinate is NaN or infinite";
+    case DBSCAN_ERR_NO_DEVICE: return "no usable gfx950 HIP device";
+    case DBSCAN_ERR_OOM: return "device memory allocation failed";
+    case DBSCAN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case DBSCAN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
+                         float eps, int32_t min_pts, int32_t* d_labels,
+                         int32_t* d_counts, void* d_workspace,
+                         size_t workspace_bytes, void* hip_stream,
+                         uint32_t flags, dbscan_info* info) {
+  if (info) std::memset(info, 0, sizeof(*info));
+  int st = check_args(n, d, eps, min_pts);
+  if (st != DBSCAN_OK) return st;
+  if (flags & ~kKnownFlags) return DBSCAN_ERR_INVALID_ARG;
+  if (n > 0 && (d_points == nullptr || d_labels == nullptr))
+    return DBSCAN_ERR_INVALID_ARG;
+  if (n == 0) return DBSCAN_OK;
+  st = have_device();
+  if (st != DBSCAN_OK) return st;
+  (void)hipGetLastError();  // launch checks below must not see older errors
+
+  Layout L{};
+  L.n = n;
+  L.d = d;
+  L.D = pick_dim(d);
+  L.stride = row_stride(L.D);
+  L.n_pad = pad_points(n);
+  if (!carve(L, d_workspace, workspace_bytes)) return DBSCAN_ERR_WORKSPACE;
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  // eps^2 rounded once in fp32, as the comparison threshold of every pair
+  volatile float eps_v = eps;
+  const float eps2 = eps_v * eps_v;
+  const bool want_edges =
+      L.edge_cap > 0 && !(flags & DBSCAN_FLAG_FORCE_TILE_MERGE);
+  PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
+  int64_t pass1 = 0, pass2 = 0;
+
+  tm.mark(0);
+  DB_TRY(launch_prepare(L, d_points, stream));
+  tm.mark(1);
+  DB_TRY(launch_count(L, eps2, want_edges, stream, &pass1));
+  tm.mark(2);
+  DB_TRY(launch_core(L, min_pts, d_counts, stream));
+
+  Status host_st;
+  DB_TRY(hipMemcpyAsync(&host_st, L.status, sizeof(Status),
+                        hipMemcpyDeviceToHost, stream));
+  DB_TRY(hipStreamSynchronize(stream));
+  if (host_st.nonfinite) return DBSCAN_ERR_NONFINITE;
+
+  const int64_t n_core = host_st.n_core;
+  const bool edges_ok = want_edges && host_st.n_edges <= L.edge_cap;
+  int mode = edges_ok ? DBSCAN_MERGE_EDGES : DBSCAN_MERGE_TILES;
+  if (!edges_ok && n_core > 0) {
+    DB_TRY(launch_compact(L, stream));
+    Status st2;
+    DB_TRY(hipMemcpyAsync(&st2, L.status, sizeof(Status),
+                          hipMemcpyDeviceToHost, stream));
+    DB_TRY(hipStreamSynchronize(stream));
+    if ((int64_t)st2.n_core_list != n_core) return DBSCAN_ERR_HIP;
+  }
+  tm.mark(3);
+  if (n_core > 0) {
+    if (edges_ok)
+      DB_TRY(launch_merge_edges(L, host_st.n_edges, stream));
+    else
+      DB_TRY(launch_merge_tiles(L, eps2, n_core, stream, &pass2));
+  }
+  tm.mark(4);
+  DB_TRY(launch_label(L, d_labels, stream));
+  tm.mark(5);
+  DB_TRY(hipStreamSynchronize(stream));
+
+  if (info) {
+    info->n_core = n_core;
+    info->n_edges = want_edges ? (int64_t)host_st.n_edges : 0;
+    info->edge_capacity = (int64_t)L.edge_cap;
+    info->pass1_pairs = pass1;
+    info->pass2_pairs = pass2;
+    info->merge_mode = mode;
+    if (tm.on) {
+      info->timed = 1;
+      info->ms_layout = tm.ms(0, 1);
+      info->ms_count = tm.ms(1, 2);
+      info->ms_core = tm.ms(2, 3);
+      info->ms_merge = tm.ms(3, 4);
+      info->ms_label = tm.ms(4, 5);
+      info->ms_total = tm.ms(0, 5);
+    }
+  }
+  return DBSCAN_OK;
+}
+
+int dbscan_fit_device(const float* d_points, int64_t n, int32_t d, float eps,
+                      int32_t min_pts, int32_t* d_labels, int32_t* d_counts,
+                      void* d_workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  return dbscan_fit_device_ex(d_points, n, d, eps, min_pts, d_labels, d_counts,
+                              d_workspace, workspace_bytes, hip_stream, 0u,
+                              nullptr);
+}
+
+int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
+               int32_t min_pts, int32_t* labels, int32_t* counts) {
+  int st = check_args(n, d, eps, min_pts);
+  if (st != DBSCAN_OK) return st;
+  if (n > 0 && (points == nullptr || labels == nullptr))
+    return DBSCAN_ERR_INVALID_ARG;
+  if (n == 0) return DBSCAN_OK;
+  st = have_device();
+  if (st != DBSCAN_OK) return st;
+
+  const size_t pts_bytes = (size_t)n * d * sizeof(float);
+  const size_t lab_bytes = (size_t)n * sizeof(int32_t);
+  const size_t ws_min = dbscan_workspace_bytes(n, d);
+  float* d_pts = nullptr;
+  int32_t* d_lab = nullptr;
+  int32_t* d_cnt = nullptr;
+  void* d_ws = nullptr;
+  size_t ws_bytes = 0;
+  hipStream_t stream = nullptr;
+  int rc = DBSCAN_OK;
+  hipError_t e = hipStreamCreate(&stream);
+  if (e != hipSuccess) return map_hip(e);
+  do {
+    if ((e = hipMalloc(&d_pts, pts_bytes)) != hipSuccess) break;
+    if ((e = hipMalloc(&d_lab, lab_bytes)) != hipSuccess) break;
+    if (counts && (e = hipMalloc(&d_cnt, lab_bytes)) != hipSuccess) break;
+    // edge area: up to a quarter of the free memory, at most 16 GiB
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) free_b = 0;
+    size_t edge_bytes = free_b / 4;
+    if (edge_bytes > ((size_t)16 << 30)) edge_bytes = (size_t)16 << 30;
+    ws_bytes = ws_min + align_up(edge_bytes, 256);
+    if (hipMalloc(&d_ws, ws_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      ws_bytes = ws_min;  // no edge area: the tile merge is used
+      if ((e = hipMalloc(&d_ws, ws_bytes)) != hipSuccess) break;
+    }
+    if ((e = hipMemcpyAsync(d_pts, points, pts_bytes, hipMemcpyHostToDevice,
+                            stream)) != hipSuccess)
+      break;
+    rc = dbscan_fit_device(d_pts, n, d, eps, min_pts, d_lab, d_cnt, d_ws,
+                           ws_bytes, stream);
+    if (rc != DBSCAN_OK) break;
+    if ((e = hipMemcpyAsync(labels, d_lab, lab_bytes, hipMemcpyDeviceToHost,
+                            stream)) != hipSuccess)
+      break;
+    if (counts && (e = hipMemcpyAsync(counts, d_cnt, lab_bytes,
+                                      hipMemcpyDeviceToHost, stream)) !=
+                      hipSuccess)
+      break;
+    e = hipStreamSynchronize(stream);
+  } while (false);
+  if (rc == DBSCAN_OK && e != hipSuccess) rc = map_hip(e);
+  (void)hipStreamSynchronize(stream);
+  if (d_ws) (void)hipFree(d_ws);
+  if (d_cnt) (void)hipFree(d_cnt);
+  if (d_lab) (void)hipFree(d_lab);
+  if (d_pts) (void)hipFree(d_pts);
+  (void)hipStreamDestroy(stream);
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device helpers: the fixed fp32 distance, wave64 primitives and the
+// lock-free union-find used by the merge kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbk {
+
+// Squared distance, dimensions in ascending order, each subtraction,
+// square and addition rounded on its own (the library is compiled with
+// -ffp-contract=off, so no multiply-add is formed).  The first square is
+// the first partial sum: adding it to +0 would return it unchanged.
+// (Wang et al., Sec. IV-A: compare the squared distance with eps^2.)
+template <int D>
+__device__ __forceinline__ float dist2(const float* a, const float* b) {
+  float t = a[0] - b[0];
+  float s = t * t;
+#pragma unroll
+  for (int k = 1; k < D; ++k) {
+    float u = a[k] - b[k];
+    float q = u * u;
+    s = s + q;
+  }
+  return s;
+}
+
+// Read-only global memory seen through the constant address space: loads
+// from wave-uniform addresses through such a pointer become scalar loads.
+typedef const float __attribute__((address_space(4)))* const_float_ptr;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+
+// Number of set bits of m below this lane.
+__device__ __forceinline__ unsigned bits_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
+// Write a wave-uniform value into one lane of a VGPR (v_writelane_b32);
+// `lane` must be wave-uniform.  gfx9 reads at most one SGPR per VALU op
+// besides M0, so the lane select is passed in M0.
+__device__ __forceinline__ int write_lane(int vgpr, int value, int lane) {
+  asm("v_writelane_b32 %0, %1, m0" : "+v"(vgpr) : "s"(value), "{m0}"(lane));
+  return vgpr;
+}
+
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
+  unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// ---- union-find over point indices ---------------------------------------
+// parent[x] <= x always: a root is only ever hung under a smaller root, and
+// path halving only replaces a parent by one of its ancestors.  Hence the
+// final root of every component is its smallest member, independent of the
+// order in which threads link, and a stale read is still an ancestor.
+// Loads are agent-scope atomics so that a spinning find never keeps
+// reading a stale value from a non-coherent cache.
+
+__device__ __forceinline__ int uf_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void uf_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline int uf_find(int* parent, int x) {
+  while (true) {
+    int p = uf_load(parent + x);
+    if (p == x) return x;
+    int g = uf_load(parent + p);
+    if (g == p) return p;
+    uf_store(parent + x, g);  // path halving
+    x = g;
+  }
+}
+
+// Link the components of a and b: CAS the larger root under the smaller.
+__device__ inline void uf_union(int* parent, int a, int b) {
+  while (true) {
+    a = uf_find(parent, a);
+    b = uf_find(parent, b);
+    if (a == b) return;
+    int hi = a > b ? a : b;
+    int lo = a > b ? b : a;
+    int old = atomicCAS(parent + hi, hi, lo);
+    if (old == hi) return;
+    // hi stopped being a root meanwhile; retry from the current ancestors
+    a = old;
+    b = lo;
+  }
+}
+
+}  // namespace dbk

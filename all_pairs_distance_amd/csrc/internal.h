@@ -1,0 +1,75 @@
+// Internal declarations shared by the library's translation units.
+// Nothing here is part of the C ABI (include/dbscan.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbk {
+
+// Point counts are padded to a multiple of this, so that every count-pass
+// variant (block sizes 256..4096 points) tiles the padded set exactly.
+constexpr int64_t kPadPoints = 4096;
+// Rows per work item of the tile passes (a multiple of the 64-lane wave).
+constexpr int kRowsPerItem = 256;
+// Edge records staged in LDS per wave before a flush to the edge area.
+constexpr int kEdgeStage = 256;
+constexpr int kThreads = 256;  // 4 waves of 64 lanes per workgroup
+constexpr int kMaxGrid = 1 << 20;
+
+// Device-side status block at the start of the workspace.
+struct Status {
+  unsigned int nonfinite;          // set to 1 if any input coordinate is NaN/inf
+  unsigned int n_core;             // number of core points
+  unsigned long long n_edges;      // edge slots reserved by the count pass
+  unsigned int n_core_list;        // entries written by the core compaction
+  unsigned int pad[11];
+};
+static_assert(sizeof(Status) == 64, "status block is 64 bytes");
+
+// Row stride of the internal point layout: d padded with zeros to the
+// compiled dimension D, then to a multiple of 4 floats (16-byte rows) when
+// D > 2 so each row is one aligned scalar/vector load.
+constexpr int row_stride(int D) { return D <= 2 ? D : ((D + 3) & ~3); }
+
+// The compiled dimensions; a fit with dimension d runs the smallest D >= d
+// (extra coordinates are 0 on both sides, which adds exact zeros to the sum).
+constexpr int kDims[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+int pick_dim(int d);  // smallest compiled D >= d, or 0
+
+struct Layout {
+  int64_t n, n_pad;
+  int d, D, stride;
+  // carved from the workspace
+  Status* status;
+  float* pts;          // [n_pad][stride], padded rows are NaN
+  unsigned* count;     // [n_pad]
+  unsigned char* core; // [n_pad]
+  int* parent;         // [n_pad] union-find forest over core points
+  int* bmin;           // [n_pad] lowest core neighbour of a non-core point
+  int* cmin;           // [n_pad] smallest member per root
+  int* core_list;      // [n_pad] compacted core indices (tile merge)
+  float* core_pts;     // [n_pad][stride] their coordinates (tile merge)
+  unsigned* block_sums;// [n_pad / 1024 + 1] compaction scan
+  uint2* edges;        // edge area (may be empty)
+  unsigned long long edge_cap;
+  size_t bytes_min;    // minimum workspace
+};
+
+size_t layout_min_bytes(int64_t n, int d);
+bool carve(Layout& L, void* ws, size_t ws_bytes);
+
+// ---- launchers (each enqueues on `s` and returns hipGetLastError) -------
+hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s);
+hipError_t launch_count(const Layout& L, float eps2, bool edges, hipStream_t s,
+                        int64_t* pairs);
+hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
+                       hipStream_t s);
+hipError_t launch_compact(const Layout& L, hipStream_t s);
+hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
+                              hipStream_t s);
+hipError_t launch_merge_tiles(const Layout& L, float eps2, int64_t n_core,
+                              hipStream_t s, int64_t* pairs);
+hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);
+
+}  // namespace dbk

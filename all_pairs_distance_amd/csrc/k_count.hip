@@ -1,0 +1,227 @@
+// Neighbour-count pass: count[i] = |{ j : d2(i,j) <= eps2 }| over all
+// ordered pairs, never storing the N x N relation.
+//
+// The relation is cut into square blocks of T = 256*P points and only the
+// upper triangle of block pairs (I <= J) is visited.  Because the fp32
+// distance is bitwise symmetric (fl(a-b) = -fl(b-a), equal squares), one
+// evaluation decides both (i,j) and (j,i): off-diagonal tiles credit the
+// row point and the column point, diagonal tiles credit only the row
+// point (every ordered pair of the block is evaluated there, the point
+// itself included).  This is the distance-matrix step of Wang et al.,
+// Sec. IV-A / IV-B1 (distance fused with the eps^2 comparison and the
+// count, nothing written per pair), restructured for a 64-lane wave:
+//   - each wave holds P column points per lane in VGPRs (the paper keeps
+//     the goal point in registers, Sec. IV-A3);
+//   - row points are wave-uniform and read with scalar loads, so the
+//     distance is one VALU op per step with an SGPR operand;
+//   - the comparison becomes a 64-bit ballot: its popcount (scalar unit) is
+//     the row point's count over 64 columns, and each lane adds its own bit
+//     for the column point (the symmetric update of the Sammon-mapping
+//     page's "modified approach").
+// Optionally every neighbour pair i<j is appended to an edge area so the
+// merge never evaluates a distance again.
+#include "device.h"
+#include "internal.h"
+
+namespace dbk {
+
+// Column points per lane: P*D coordinates + P counters stay in VGPRs.
+constexpr int lane_points(int D) {
+  return D <= 2 ? 16 : D <= 4 ? 8 : D <= 8 ? 4 : D <= 16 ? 2 : 1;
+}
+
+// Upper-triangle tile t (row-major over I <= J of nb x nb blocks) -> (I, J).
+__device__ __forceinline__ void tile_coords(int64_t t, int64_t nb, int64_t& I,
+                                            int64_t& J) {
+  const double b = 2.0 * (double)nb + 1.0;
+  int64_t i = (int64_t)((b - sqrt(b * b - 8.0 * (double)t)) * 0.5);
+  if (i < 0) i = 0;
+  if (i > nb - 1) i = nb - 1;
+  while (i > 0 && i * nb - i * (i - 1) / 2 > t) --i;
+  while (i + 1 < nb && (i + 1) * nb - (i + 1) * i / 2 <= t) ++i;
+  I = i;
+  J = i + (t - (i * nb - i * (i - 1) / 2));
+}
+
+struct EdgeSink {
+  uint2* edges;
+  unsigned long long cap;
+  unsigned long long* counter;
+};
+
+// Order this wave's LDS accesses around a hand-over between lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Copy the wave's staged edges to the edge area (one atomic per flush).
+// Slots past the capacity are dropped; the host sees the overflow because
+// the counter then exceeds the capacity.
+__device__ __noinline__ void flush_edges(uint2* stage, unsigned fill,
+                                         const EdgeSink& sink) {
+  wave_lds_sync();
+  unsigned long long base = 0;
+  if (lane_id() == 0) base = atomicAdd(sink.counter, (unsigned long long)fill);
+  base = uniform_u64(base);
+  for (unsigned k = lane_id(); k < fill; k += 64) {
+    const unsigned long long dst = base + k;
+    if (dst < sink.cap) sink.edges[dst] = stage[k];
+  }
+  wave_lds_sync();
+}
+
+// Stage the pairs (row, col0 + lane) of mask m; on a diagonal tile only the
+// pairs with col > row (each unordered pair once, never (i,i)).
+template <bool DIAG>
+__device__ __forceinline__ void stage_edges(uint64_t m, int64_t row,
+                                            int64_t col0, uint2* stage,
+                                            unsigned& fill,
+                                            const EdgeSink& sink) {
+  if (DIAG) {
+    const int64_t first = row - col0 + 1;
+    if (first >= 64) return;
+    if (first > 0) m &= ~0ull << first;
+  }
+  if (m == 0) return;
+  const unsigned cnt = (unsigned)__popcll(m);
+  if (fill + cnt > (unsigned)kEdgeStage) {
+    flush_edges(stage, fill, sink);
+    fill = 0;
+  }
+  const int lane = lane_id();
+  if ((m >> lane) & 1ull)
+    stage[fill + bits_below(m)] =
+        make_uint2((unsigned)row, (unsigned)(col0 + lane));
+  fill += cnt;
+}
+
+// One work item: `rows` consecutive row points against this wave's 64*P
+// column points.
+template <int D, int P, bool DIAG, bool EDGES>
+__device__ __forceinline__ void count_item(const float* __restrict__ pts,
+                                           int64_t row0, int rows,
+                                           int64_t colw, float eps2,
+                                           unsigned* __restrict__ count,
+                                           uint2* stage, unsigned& fill,
+                                           const EdgeSink& sink) {
+  constexpr int S = row_stride(D);
+  const int lane = lane_id();
+  float xc[P][D];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const float* cp = pts + (colw + p * 64 + lane) * S;
+#pragma unroll
+    for (int k = 0; k < D; ++k) xc[p][k] = cp[k];
+  }
+  unsigned lc[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) lc[p] = 0;
+
+  for (int rb = 0; rb < rows; rb += 64) {
+    int rowv = 0;  // lane l: count of row rb+l over these columns
+#pragma unroll 2
+    for (int l = 0; l < 64; ++l) {
+      const int64_t row = row0 + rb + l;
+      // wave-uniform address: read through the constant address space so
+      // the row lands in SGPRs via scalar loads
+      const const_float_ptr rp = (const_float_ptr)(pts + row * S);
+      float xr[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k) xr[k] = rp[k];
+      unsigned acc = 0;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const float s = dist2<D>(xr, xc[p]);
+        const bool nb = s <= eps2;
+        const uint64_t m = ballot(nb);
+        acc += (unsigned)__popcll(m);
+        if (!DIAG) lc[p] += nb ? 1u : 0u;
+        if (EDGES) stage_edges<DIAG>(m, row, colw + p * 64, stage, fill, sink);
+      }
+      rowv = write_lane(rowv, (int)acc, l);
+    }
+    if (rowv) atomicAdd(count + row0 + rb + lane, (unsigned)rowv);
+  }
+  if (!DIAG) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (lc[p]) atomicAdd(count + colw + p * 64 + lane, lc[p]);
+  }
+}
+
+template <int D, bool EDGES>
+__global__ __launch_bounds__(kThreads) void k_count(
+    const float* __restrict__ pts, int64_t nb, int chunks_log2, int rows,
+    int64_t items, float eps2, unsigned* __restrict__ count,
+    uint2* __restrict__ edges, unsigned long long cap,
+    unsigned long long* __restrict__ counter) {
+  constexpr int P = lane_points(D);
+  constexpr int T = 256 * P;
+  __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  uint2* stage = stage_all + (EDGES ? wave * kEdgeStage : 0);
+  unsigned fill = 0;
+  const EdgeSink sink{edges, cap, counter};
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t tile = item >> chunks_log2;
+    const int c = (int)(item & ((1 << chunks_log2) - 1));
+    int64_t I, J;
+    tile_coords(tile, nb, I, J);
+    const int64_t row0 = I * T + (int64_t)c * rows;
+    const int64_t colw = J * T + (int64_t)wave * 64 * P;
+    if (I == J)
+      count_item<D, P, true, EDGES>(pts, row0, rows, colw, eps2, count, stage,
+                                    fill, sink);
+    else
+      count_item<D, P, false, EDGES>(pts, row0, rows, colw, eps2, count,
+                                     stage, fill, sink);
+  }
+  if (EDGES && fill) flush_edges(stage, fill, sink);
+}
+
+template <int D>
+static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
+                                 hipStream_t s, int64_t* pairs) {
+  constexpr int P = lane_points(D);
+  constexpr int T = 256 * P;
+  const int64_t nb = L.n_pad / T;
+  const int rows = kRowsPerItem < T ? kRowsPerItem : T;
+  const int chunks = T / rows;  // both powers of two
+  int chunks_log2 = 0;
+  while ((1 << chunks_log2) < chunks) ++chunks_log2;
+  const int64_t items = nb * (nb + 1) / 2 * chunks;
+  const unsigned grid = (unsigned)(items < kMaxGrid ? items : kMaxGrid);
+  if (edges)
+    k_count<D, true><<<grid, kThreads, 0, s>>>(
+        L.pts, nb, chunks_log2, rows, items, eps2, L.count, L.edges, L.edge_cap,
+        &L.status->n_edges);
+  else
+    k_count<D, false><<<grid, kThreads, 0, s>>>(
+        L.pts, nb, chunks_log2, rows, items, eps2, L.count, nullptr, 0ull,
+        &L.status->n_edges);
+  if (pairs) *pairs = L.n_pad * L.n_pad;
+  return hipGetLastError();
+}
+
+hipError_t launch_count(const Layout& L, float eps2, bool edges, hipStream_t s,
+                        int64_t* pairs) {
+  switch (L.D) {
+    case 1: return launch_count_d<1>(L, eps2, edges, s, pairs);
+    case 2: return launch_count_d<2>(L, eps2, edges, s, pairs);
+    case 3: return launch_count_d<3>(L, eps2, edges, s, pairs);
+    case 4: return launch_count_d<4>(L, eps2, edges, s, pairs);
+    case 6: return launch_count_d<6>(L, eps2, edges, s, pairs);
+    case 8: return launch_count_d<8>(L, eps2, edges, s, pairs);
+    case 12: return launch_count_d<12>(L, eps2, edges, s, pairs);
+    case 16: return launch_count_d<16>(L, eps2, edges, s, pairs);
+    case 24: return launch_count_d<24>(L, eps2, edges, s, pairs);
+    case 32: return launch_count_d<32>(L, eps2, edges, s, pairs);
+    case 48: return launch_count_d<48>(L, eps2, edges, s, pairs);
+    case 64: return launch_count_d<64>(L, eps2, edges, s, pairs);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dbk

@@ -1,0 +1,232 @@
+// Bandwidth-bound passes around the two distance passes: ingest/layout,
+// core flags (+ sorted compaction for the tile merge), root compression
+// and canonical labels.  Each is a grid-stride loop over points with
+// coalesced loads and stores.
+#include <climits>
+
+#include "device.h"
+#include "internal.h"
+
+namespace dbk {
+
+static unsigned grid_for(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (unsigned)(g < kMaxGrid ? g : kMaxGrid);
+}
+
+__global__ void k_zero_status(Status* st) {
+  unsigned* w = reinterpret_cast<unsigned*>(st);
+  if (threadIdx.x < sizeof(Status) / 4) w[threadIdx.x] = 0u;
+}
+
+// Copy the caller's [n][d] points into the padded [n_pad][S] layout: the
+// coordinates d..S-1 of a real point are 0 (adding 0 to a sum of squares
+// is exact), every coordinate of a padding row is NaN (never a neighbour
+// of anything).  Flags any non-finite input coordinate.
+__global__ void k_layout(const float* __restrict__ in, int64_t n, int d, int S,
+                         int64_t total, float* __restrict__ pts,
+                         Status* __restrict__ st) {
+  bool bad = false;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / S;
+    const int k = (int)(e - i * S);
+    float v;
+    if (i < n) {
+      v = k < d ? in[i * d + k] : 0.0f;
+      bad |= !__builtin_isfinite(v);
+    } else {
+      v = __builtin_nanf("");
+    }
+    pts[e] = v;
+  }
+  if (bad) st->nonfinite = 1u;
+}
+
+__global__ void k_init_points(int64_t n_pad, unsigned* __restrict__ count,
+                              int* __restrict__ parent, int* __restrict__ bmin,
+                              int* __restrict__ cmin) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    count[i] = 0u;
+    parent[i] = (int)i;
+    bmin[i] = INT_MAX;
+    cmin[i] = INT_MAX;
+  }
+}
+
+hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s) {
+  k_zero_status<<<1, 64, 0, s>>>(L.status);
+  const int64_t total = L.n_pad * L.stride;
+  k_layout<<<grid_for(total, 256 * 8), 256, 0, s>>>(in, L.n, L.d, L.stride,
+                                                     total, L.pts, L.status);
+  k_init_points<<<grid_for(L.n_pad, 256 * 4), 256, 0, s>>>(
+      L.n_pad, L.count, L.parent, L.bmin, L.cmin);
+  return hipGetLastError();
+}
+
+// core[i] = count[i] >= min_pts (Wang et al., Sec. II item 2: at least
+// MinPts points within eps); copies the counts out if asked.
+__global__ void k_core(const unsigned* __restrict__ count, int64_t n,
+                       int64_t n_pad, int min_pts,
+                       unsigned char* __restrict__ core,
+                       int* __restrict__ counts_out, Status* __restrict__ st) {
+  unsigned mine = 0;
+  // n_pad is a multiple of the block size, so whole waves enter together
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const unsigned c = count[i];
+    const bool is_core = i < n && c >= (unsigned)min_pts;
+    core[i] = is_core ? 1 : 0;
+    if (counts_out && i < n) counts_out[i] = (int)c;
+    mine += (unsigned)__popcll(ballot(is_core));
+  }
+  if (lane_id() == 0 && mine) atomicAdd(&st->n_core, mine);
+}
+
+hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
+                       hipStream_t s) {
+  k_core<<<grid_for(L.n_pad, 256 * 4), 256, 0, s>>>(
+      L.count, L.n, L.n_pad, min_pts, L.core, counts_out, L.status);
+  return hipGetLastError();
+}
+
+// ---- sorted compaction of the core points (tile merge only) --------------
+// Blocks of 1024 points: per-block core totals, one exclusive scan over
+// the totals, then each block writes its cores in index order.
+
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh,
+                                                    unsigned* total) {
+  // 256 threads = 4 waves
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  unsigned x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    unsigned y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  unsigned wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += sh[w];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return wbase + x - v;
+}
+
+__global__ __launch_bounds__(256) void k_core_block_totals(
+    const unsigned char* __restrict__ core, int64_t n_pad,
+    unsigned* __restrict__ sums) {
+  __shared__ unsigned sh[4];
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
+  unsigned c = 0;
+  if (base < n_pad)
+    c = core[base] + core[base + 1] + core[base + 2] + core[base + 3];
+  unsigned tot;
+  block_excl_scan(c, sh, &tot);
+  if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+// Exclusive scan of the block totals in place, by one workgroup.
+__global__ __launch_bounds__(256) void k_scan_totals(unsigned* sums,
+                                                     int64_t nblk,
+                                                     Status* st) {
+  __shared__ unsigned sh[4];
+  unsigned carry = 0;
+  for (int64_t b0 = 0; b0 < nblk; b0 += 256) {
+    const int64_t b = b0 + threadIdx.x;
+    const unsigned v = b < nblk ? sums[b] : 0u;
+    unsigned tot;
+    const unsigned ex = block_excl_scan(v, sh, &tot);
+    if (b < nblk) sums[b] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) st->n_core_list = carry;
+}
+
+__global__ __launch_bounds__(256) void k_core_scatter(
+    const unsigned char* __restrict__ core, const float* __restrict__ pts,
+    int64_t n_pad, int S, const unsigned* __restrict__ sums,
+    int* __restrict__ core_list, float* __restrict__ core_pts) {
+  __shared__ unsigned sh[4];
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
+  unsigned f[4] = {0, 0, 0, 0};
+  if (base < n_pad)
+    for (int q = 0; q < 4; ++q) f[q] = core[base + q];
+  unsigned tot;
+  unsigned pos = sums[blockIdx.x] +
+                 block_excl_scan(f[0] + f[1] + f[2] + f[3], sh, &tot);
+  for (int q = 0; q < 4; ++q) {
+    if (f[q]) {
+      const int64_t i = base + q;
+      core_list[pos] = (int)i;
+      for (int k = 0; k < S; ++k) core_pts[(int64_t)pos * S + k] = pts[i * S + k];
+      ++pos;
+    }
+  }
+}
+
+__global__ void k_fill_nan(float* __restrict__ p, int64_t total) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = __builtin_nanf("");
+}
+
+hipError_t launch_compact(const Layout& L, hipStream_t s) {
+  const int64_t nblk = L.n_pad / 1024;
+  k_fill_nan<<<grid_for(L.n_pad * L.stride, 256 * 8), 256, 0, s>>>(
+      L.core_pts, L.n_pad * L.stride);
+  k_core_block_totals<<<(unsigned)nblk, 256, 0, s>>>(L.core, L.n_pad,
+                                                      L.block_sums);
+  k_scan_totals<<<1, 256, 0, s>>>(L.block_sums, nblk, L.status);
+  k_core_scatter<<<(unsigned)nblk, 256, 0, s>>>(
+      L.core, L.pts, L.n_pad, L.stride, L.block_sums, L.core_list,
+      L.core_pts);
+  return hipGetLastError();
+}
+
+// ---- labels ----------------------------------------------------------------
+// Every core point finds its root (the smallest core of its component); a
+// border point takes the root of its lowest-index core neighbour.  Each
+// root collects the smallest member index with atomicMin; that index is
+// the cluster's label.  Roots are kept in bmin[] (unused for cores until
+// now) so the label pass needs no further pointer chasing.
+__global__ void k_finalize(int64_t n, const unsigned char* __restrict__ core,
+                           int* __restrict__ parent, int* __restrict__ bmin,
+                           int* __restrict__ cmin) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int r;
+    if (core[i]) {
+      r = uf_find(parent, (int)i);
+    } else {
+      const int b = bmin[i];
+      if (b == INT_MAX) continue;
+      r = uf_find(parent, b);
+    }
+    bmin[i] = r;
+    atomicMin(cmin + r, (int)i);
+  }
+}
+
+__global__ void k_write_labels(int64_t n, const unsigned char* __restrict__ core,
+                               const int* __restrict__ bmin,
+                               const int* __restrict__ cmin,
+                               int* __restrict__ labels) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int r = bmin[i];
+    labels[i] = r == INT_MAX ? -1 : cmin[r];
+  }
+}
+
+hipError_t launch_label(const Layout& L, int* labels, hipStream_t s) {
+  k_finalize<<<grid_for(L.n, 256 * 4), 256, 0, s>>>(L.n, L.core, L.parent,
+                                                    L.bmin, L.cmin);
+  k_write_labels<<<grid_for(L.n, 256 * 4), 256, 0, s>>>(L.n, L.core, L.bmin,
+                                                        L.cmin, labels);
+  return hipGetLastError();
+}
+
+}  // namespace dbk

@@ -1,0 +1,154 @@
+/*
+ * dbscan.h -- exact all-pairs DBSCAN on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  No exception, C++ type or torch type crosses it; every argument
+ * is a plain pointer (host or device, as stated) or a size.
+ *
+ * What a fit computes (Wang et al., "Design and optimization of DBSCAN
+ * Algorithm based on CUDA", Sec. II: epsilon-neighbourhood, core point,
+ * reachability and the two-part cluster definition; Sec. IV-A: compare the
+ * squared distance with eps^2), with these fixed readings:
+ *   - d2(i,j) = sum over k = 0..d-1, in that order, of fl(fl(x_ik - x_jk)^2),
+ *     each operation an IEEE binary32 round-to-nearest-even step (no fused
+ *     multiply-add, subnormals kept); eps2 = fl(eps * eps);
+ *   - N(i) = { j : d2(i,j) <= eps2 }, i itself included; count[i] = |N(i)|;
+ *   - i is a core point iff count[i] >= min_pts;
+ *   - clusters are the connected components of the graph whose vertices are
+ *     the core points, with an edge between two cores within eps;
+ *   - a non-core point with at least one core neighbour (a border point)
+ *     joins the cluster of its lowest-index core neighbour;
+ *   - every other point is noise, label -1;
+ *   - a cluster's label is the smallest point index among its members
+ *     (its cores and the border points it received).
+ * The result is unique, so labels and counts are bit-for-bit reproducible
+ * whatever the launch order on the GPU.
+ *
+ * Points are row-major fp32: point i occupies points[i*d .. i*d+d-1].
+ * 0 <= n <= 2^31-1, 1 <= d <= DBSCAN_MAX_D, eps finite and >= 0,
+ * min_pts >= 1.  n = 0 is a successful no-op.
+ */
+#ifndef DBSCAN_MI355X_H
+#define DBSCAN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBSCAN_ABI_VERSION 1
+#define DBSCAN_MAX_D 64
+
+/* Status codes: 0 on success, negative on failure.  On any failure the
+ * contents of labels / counts are unspecified.  Argument errors are
+ * reported before any device work is enqueued. */
+typedef enum dbscan_status {
+  DBSCAN_OK = 0,
+  DBSCAN_ERR_INVALID_ARG = -1, /* n<0 or n>2^31-1, d<1 or d>DBSCAN_MAX_D,
+                                  eps NaN/inf/negative, min_pts<1, a NULL
+                                  pointer where n>0, unknown flag bits */
+  DBSCAN_ERR_NONFINITE = -2,   /* a coordinate is NaN or +-inf */
+  DBSCAN_ERR_NO_DEVICE = -3,   /* no HIP device, or the current device is
+                                  not gfx950 */
+  DBSCAN_ERR_OOM = -4,         /* dbscan_fit only: device allocation failed */
+  DBSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than
+                                  dbscan_workspace_bytes(n, d), or misaligned */
+  DBSCAN_ERR_HIP = -6          /* any other HIP runtime error */
+} dbscan_status;
+
+/* Merge strategies a fit may take (reported in dbscan_info.merge_mode). */
+#define DBSCAN_MERGE_NONE 0  /* n == 0 */
+#define DBSCAN_MERGE_EDGES 1 /* the count pass recorded every neighbour pair
+                                (i<j) in the workspace's edge area, and the
+                                merge walked that list: no distance is
+                                evaluated twice */
+#define DBSCAN_MERGE_TILES 2 /* the edge area was absent or too small: the
+                                merge re-evaluated distances in a second tile
+                                pass over (all points) x (core points) */
+
+/* Flag bits for dbscan_fit_device_ex. */
+#define DBSCAN_FLAG_TIME_PHASES 0x1u  /* fill the ms_* fields of dbscan_info
+                                         from HIP events on the stream */
+#define DBSCAN_FLAG_FORCE_TILE_MERGE 0x2u /* ignore the edge area and take the
+                                             tile merge (for testing) */
+
+/* What a fit did; filled by dbscan_fit_device_ex when info != NULL. */
+typedef struct dbscan_info {
+  int64_t n_core;        /* number of core points */
+  int64_t n_edges;       /* neighbour pairs i<j found by the count pass (0
+                            when no edge area was given) */
+  int64_t edge_capacity; /* pairs the edge area can hold */
+  int64_t pass1_pairs;   /* ordered pairs (i,j) decided by the count pass,
+                            including padding: n_pad^2 */
+  int64_t pass2_pairs;   /* distances evaluated by a tile merge (0 for the
+                            edge merge) */
+  int32_t merge_mode;    /* DBSCAN_MERGE_* */
+  int32_t timed;         /* 1 if the ms_* fields below were measured */
+  float ms_layout;       /* ingest, padding, non-finite check, init */
+  float ms_count;        /* neighbour-count pass */
+  float ms_core;         /* core flags (+ core compaction for a tile merge) */
+  float ms_merge;        /* union-find merge and border assignment */
+  float ms_label;        /* root compression and canonical labels */
+  float ms_total;        /* first to last kernel of the fit */
+  int32_t hip_error;     /* hipError_t of the failing HIP call, 0 if none */
+  int32_t reserved;
+} dbscan_info;
+
+/* Minimum workspace (bytes) for dbscan_fit_device with n points of
+ * dimension d; 0 if n or d is out of range. */
+size_t dbscan_workspace_bytes(int64_t n, int32_t d);
+
+/* Workspace (bytes) that also holds an edge area for max_edges neighbour
+ * pairs: dbscan_workspace_bytes(n, d) + 8 * max_edges, rounded up. */
+size_t dbscan_workspace_bytes_with_edges(int64_t n, int32_t d,
+                                         int64_t max_edges);
+
+/* Fit from device memory, stream-ordered.
+ *   d_points   device, n*d fp32, row-major; read only; caller-owned.
+ *   d_labels   device, n int32; written; caller-owned.
+ *   d_counts   device, n int32 neighbour counts (self included), or NULL.
+ *   d_workspace, workspace_bytes  device scratch owned by the caller, at
+ *              least dbscan_workspace_bytes(n, d), 256-byte aligned.  Bytes
+ *              beyond that minimum become the edge area (8 bytes per pair);
+ *              when every neighbour pair fits there the merge reuses them,
+ *              otherwise it re-evaluates distances (same result, slower).
+ *   hip_stream hipStream_t passed as void*; NULL = the default stream.
+ * All kernels run on hip_stream.  The call synchronises that stream
+ * (twice: once to size the merge, once at the end) so the returned status
+ * is final; it is not capturable into a HIP graph.  Calls on different
+ * streams with different workspaces may run concurrently; two calls must
+ * not share a workspace at the same time.  The library keeps no state
+ * between calls. */
+int dbscan_fit_device(const float* d_points, int64_t n, int32_t d, float eps,
+                      int32_t min_pts, int32_t* d_labels, int32_t* d_counts,
+                      void* d_workspace, size_t workspace_bytes,
+                      void* hip_stream);
+
+/* As dbscan_fit_device, with flag bits (DBSCAN_FLAG_*) and an optional host
+ * dbscan_info to fill (NULL allowed). */
+int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
+                         float eps, int32_t min_pts, int32_t* d_labels,
+                         int32_t* d_counts, void* d_workspace,
+                         size_t workspace_bytes, void* hip_stream,
+                         uint32_t flags, dbscan_info* info);
+
+/* Fit from host memory: allocates device memory (points, labels, counts,
+ * workspace with an edge area sized from free device memory), copies in,
+ * fits on a stream of its own, copies out and frees everything before
+ * returning.  labels: host, n int32.  counts: host, n int32, or NULL.
+ * Blocking. */
+int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
+               int32_t min_pts, int32_t* labels, int32_t* counts);
+
+/* Static, never-NULL description of a status code. */
+const char* dbscan_status_string(int status);
+
+/* DBSCAN_ABI_VERSION of the loaded library. */
+int dbscan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBSCAN_MI355X_H */

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads,
+exports every function include/dbscan.h declares, sizes workspaces
+consistently and rejects bad arguments before touching a device."""
+import ctypes
+import re
+
+import numpy as np
+import pytest
+
+from all_pairs_distance_amd import _capi
+import all_pairs_distance_amd as apd
+
+
+def declared_functions():
+    text = open(_capi.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(dbscan_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("dbscan_fit", "dbscan_fit_device", "dbscan_fit_device_ex",
+                 "dbscan_workspace_bytes", "dbscan_workspace_bytes_with_edges",
+                 "dbscan_status_string", "dbscan_abi_version"):
+        assert want in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_declared_symbol(name):
+    lib = ctypes.CDLL(_capi.LIB_PATH)
+    assert hasattr(lib, name)
+    assert hasattr(_capi, name)      # the binding keeps the C names
+
+
+def test_abi_version_and_constants():
+    text = open(_capi.HEADER_PATH).read()
+    ver = int(re.search(r"#define DBSCAN_ABI_VERSION (\d+)", text).group(1))
+    assert apd.dbscan_abi_version() == ver
+    assert int(re.search(r"#define DBSCAN_MAX_D (\d+)", text).group(1)) == _capi.MAX_D
+    for name, value in re.findall(r"(DBSCAN_ERR_[A-Z_]+|DBSCAN_OK) = (-?\d+)", text):
+        assert getattr(_capi, name.replace("DBSCAN_", "")) == int(value)
+    for name, value in re.findall(r"#define DBSCAN_(MERGE_[A-Z]+|FLAG_[A-Z_]+) (0x[0-9a-f]+u?|\d+)", text):
+        assert getattr(_capi, name) == int(value.rstrip("u"), 0)
+
+
+def test_info_struct_matches_header_layout():
+    # 5 int64, 2 int32, 6 float, 2 int32
+    assert ctypes.sizeof(_capi.dbscan_info) == 5 * 8 + 2 * 4 + 6 * 4 + 2 * 4
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert isinstance(apd.dbscan_status_string(s), str)
+    assert apd.dbscan_status_string(0) == "ok"
+    assert "unknown" in apd.dbscan_status_string(12345)
+
+
+def test_workspace_sizes():
+    assert apd.dbscan_workspace_bytes(1000, 0) == 0
+    assert apd.dbscan_workspace_bytes(1000, 65) == 0
+    assert apd.dbscan_workspace_bytes(-1, 3) == 0
+    assert apd.dbscan_workspace_bytes(2 ** 31, 3) == 0
+    prev = 0
+    for n in (0, 1, 4096, 4097, 10 ** 6):
+        b = apd.dbscan_workspace_bytes(n, 3)
+        assert b > 0 and b >= prev and b % 256 == 0
+        prev = b
+    # all dimensions that share a padded stride share a size
+    assert apd.dbscan_workspace_bytes(5000, 3) == apd.dbscan_workspace_bytes(5000, 4)
+    assert apd.dbscan_workspace_bytes(5000, 5) > apd.dbscan_workspace_bytes(5000, 4)
+    base = apd.dbscan_workspace_bytes(5000, 8)
+    assert apd.dbscan_workspace_bytes_with_edges(5000, 8, 0) == base
+    assert apd.dbscan_workspace_bytes_with_edges(5000, 8, 1000) >= base + 8000
+    assert apd.dbscan_workspace_bytes_with_edges(5000, 8, -1) == 0
+
+
+def _status(points, n, d, eps, m, labels=True):
+    lab = np.empty(max(n, 1), np.int32)
+    return apd.dbscan_fit(points.ctypes.data if points is not None else None,
+                          n, d, eps, m, lab.ctypes.data if labels else None, None)
+
+
+def test_invalid_arguments_rejected_before_device_work():
+    x = np.zeros((8, 2), np.float32)
+    assert _status(x, 8, 2, 0.1, 0) == _capi.ERR_INVALID_ARG
+    assert _status(x, 8, 0, 0.1, 1) == _capi.ERR_INVALID_ARG
+    assert _status(x, 8, 65, 0.1, 1) == _capi.ERR_INVALID_ARG
+    assert _status(x, -1, 2, 0.1, 1) == _capi.ERR_INVALID_ARG
+    assert _status(x, 2 ** 31, 2, 0.1, 1) == _capi.ERR_INVALID_ARG
+    assert _status(x, 8, 2, -0.5, 1) == _capi.ERR_INVALID_ARG
+    assert _status(x, 8, 2, float("nan"), 1) == _capi.ERR_INVALID_ARG
+    assert _status(x, 8, 2, float("inf"), 1) == _capi.ERR_INVALID_ARG
+    assert _status(None, 8, 2, 0.1, 1) == _capi.ERR_INVALID_ARG
+    assert _status(x, 8, 2, 0.1, 1, labels=False) == _capi.ERR_INVALID_ARG
+    assert _status(None, 0, 2, 0.1, 1, labels=False) == _capi.OK
+    ws = np.zeros(16, np.uint8)
+    st = apd.dbscan_fit_device_ex(x.ctypes.data, 8, 2, 0.1, 1, ws.ctypes.data,
+                                  None, ws.ctypes.data, 16, None, 0x80, None)
+    assert st == _capi.ERR_INVALID_ARG               # unknown flag bit
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="a GPU is visible")
+def test_no_device_reported():
+    x = np.zeros((8, 2), np.float32)
+    assert _status(x, 8, 2, 0.1, 1) == _capi.ERR_NO_DEVICE
+    with pytest.raises(apd.DbscanError) as e:
+        apd.fit_host(x, 0.1, 1)
+    assert e.value.status == _capi.ERR_NO_DEVICE

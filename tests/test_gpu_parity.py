@@ -1,0 +1,271 @@
+"""Parity of the HIP library (through the C ABI) with the brute-force oracle.
+
+Labels and neighbour counts must be bit-identical.  Small and medium inputs
+are compared element by element with a live oracle run; the five named
+workloads at full size are compared with the oracle's stored SHA-256
+digests (tests/golden/workloads.json, written by the oracle alone), with
+sampled rows recomputed live by the oracle and with label invariants on
+sampled points.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import pins
+from all_pairs_distance_amd import datagen
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN_WORKLOADS = os.path.join(pins.GOLDEN, "workloads.json")
+
+
+@pytest.fixture(scope="module")
+def apd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible gfx950 device"
+    import all_pairs_distance_amd
+    return all_pairs_distance_amd
+
+
+def gpu_fit(apd, x, eps, m, flags=0, max_edges=None):
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x.reshape(-1, 1)
+    n = x.shape[0]
+    if max_edges is None:
+        max_edges = max(1, min(n * (n - 1) // 2, 1 << 28))
+    t = torch.from_numpy(x).cuda()
+    labels, counts, info = apd.fit(t, eps, m, return_counts=True, flags=flags,
+                                   max_edges=max_edges, return_info=True)
+    torch.cuda.synchronize()
+    return labels.cpu().numpy(), counts.cpu().numpy(), info
+
+
+def assert_same(got_l, got_c, want_l, want_c, what):
+    bad_c = np.nonzero(got_c != want_c)[0]
+    assert bad_c.size == 0, f"{what}: {bad_c.size} counts differ, first {bad_c[:5]}"
+    bad_l = np.nonzero(got_l != want_l)[0]
+    assert bad_l.size == 0, f"{what}: {bad_l.size} labels differ, first {bad_l[:5]}"
+
+
+MODES = [(0, "edges"), (2, "tiles")]   # 2 = FLAG_FORCE_TILE_MERGE
+
+
+@pytest.mark.parametrize("flags,mode", MODES, ids=[m for _, m in MODES])
+def test_handworked(apd, flags, mode):
+    for cid, pts, eps, m, counts, labels in pins.load_handworked():
+        lab, cnt, info = gpu_fit(apd, pts, eps, m, flags=flags)
+        assert_same(lab, cnt, labels, counts, cid)
+
+
+@pytest.mark.parametrize("flags,mode", MODES, ids=[m for _, m in MODES])
+def test_small_random_vs_oracle(apd, orc, flags, mode):
+    for t, (x, eps, m) in enumerate(pins.small_cases(seed=101, count=80)):
+        want_l, want_c, _ = orc.fit(x, eps, m)
+        lab, cnt, info = gpu_fit(apd, x, eps, m, flags=flags)
+        assert_same(lab, cnt, want_l, want_c, f"case {t} n={x.shape} eps={eps} m={m}")
+        if x.shape[0] > 0 and info["n_core"] > 0:
+            want_mode = 2 if flags else 1
+            assert info["merge_mode"] == want_mode
+
+
+SIZES = [1, 2, 63, 64, 65, 255, 257, 4095, 4096, 4097, 8191, 12289]
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_tiles_and_ragged_tails(apd, orc, n):
+    for d in (1, 2, 3, 5, 8, 13, 33, 64):
+        x = datagen.gaussian_blobs(n, d, seed=1000 * n + d, n_blobs=5,
+                                   sigma=0.03, noise_frac=0.2)
+        eps = 0.05 * np.sqrt(d)
+        want_l, want_c, _ = orc.fit(x, eps, 4)
+        for flags, mode in MODES:
+            lab, cnt, _ = gpu_fit(apd, x, eps, 4, flags=flags)
+            assert_same(lab, cnt, want_l, want_c, f"n={n} d={d} {mode}")
+
+
+def test_every_dimension(apd, orc):
+    """Every d in 1..64: the compiled widths and the zero-padded ones."""
+    for d in range(1, 65):
+        x = datagen.gaussian_blobs(3000, d, seed=77 + d, n_blobs=6, sigma=0.02,
+                                   noise_frac=0.1)
+        eps = 0.04 * np.sqrt(d)
+        want_l, want_c, _ = orc.fit(x, eps, 5)
+        lab, cnt, _ = gpu_fit(apd, x, eps, 5)
+        assert_same(lab, cnt, want_l, want_c, f"d={d}")
+
+
+def test_boundary_ties(apd, orc):
+    """Distances that land exactly on eps^2, or one ulp either side."""
+    x = datagen.collinear_chain(4000, 0.03)               # fl32(k * 0.03)
+    for eps in (0.03, float(np.nextafter(np.float32(0.03), np.float32(1))),
+                float(np.nextafter(np.float32(0.03), np.float32(0)))):
+        want_l, want_c, _ = orc.fit(x, eps, 2)
+        lab, cnt, _ = gpu_fit(apd, x, eps, 2)
+        assert_same(lab, cnt, want_l, want_c, f"chain eps={eps!r}")
+    lat = datagen.integer_lattice(40, 2)
+    for eps, m in ((1.0, 5), (1.0, 4), (2.0 ** 0.5, 9), (0.0, 1)):
+        want_l, want_c, _ = orc.fit(lat, eps, m)
+        lab, cnt, _ = gpu_fit(apd, lat, eps, m)
+        assert_same(lab, cnt, want_l, want_c, f"lattice eps={eps} m={m}")
+    # subnormal squared differences are kept, not flushed
+    x = np.array([[0.0], [1e-20], [3e-20]], np.float32)
+    lab, cnt, _ = gpu_fit(apd, x, 0.0, 1)
+    assert cnt.tolist() == [1, 1, 1] and lab.tolist() == [0, 1, 2]
+
+
+def test_degenerate_inputs(apd, orc):
+    same = np.ones((5000, 3), np.float32) * np.float32(0.25)
+    lab, cnt, _ = gpu_fit(apd, same, 0.0, 5000)
+    assert np.all(cnt == 5000) and np.all(lab == 0)
+    lab, cnt, _ = gpu_fit(apd, same, 0.0, 5001)
+    assert np.all(lab == -1)
+    # a long chain: deep union-find paths, every point core
+    chain = datagen.collinear_chain(100000, 0.5)
+    lab, cnt, _ = gpu_fit(apd, chain, 0.5, 2)
+    want_c = np.full(100000, 3, np.int32)
+    want_c[[0, -1]] = 2
+    assert np.array_equal(cnt, want_c) and np.all(lab == 0)
+    lab, cnt, _ = gpu_fit(apd, chain, 0.5, 2, flags=2)
+    assert np.array_equal(cnt, want_c) and np.all(lab == 0)
+    # reversed chain: the smallest index sits at the far end
+    rev = np.ascontiguousarray(chain[::-1])
+    lab, _, _ = gpu_fit(apd, rev, 0.5, 3)
+    assert lab[0] == 0 and lab[-1] == 0 and np.all(lab == 0)
+    # MinPts = 1 and a radius larger than the diameter
+    x = datagen.uniform_points(20000, 2, 5)
+    lab, cnt, _ = gpu_fit(apd, x, 2.0, 1)
+    assert np.all(cnt == 20000) and np.all(lab == 0)
+    x = datagen.uniform_points(3000, 3, 6)
+    want_l, want_c, _ = orc.fit(x, 0.05, 1)
+    lab, cnt, _ = gpu_fit(apd, x, 0.05, 1)
+    assert_same(lab, cnt, want_l, want_c, "minpts 1")
+
+
+def test_edge_area_overflow_falls_back(apd, orc):
+    x = datagen.gaussian_blobs(20000, 2, seed=3, n_blobs=4, sigma=0.05)
+    want_l, want_c, _ = orc.fit(x, 0.02, 8)
+    for cap in (0, 1, 1000):
+        lab, cnt, info = gpu_fit(apd, x, 0.02, 8, max_edges=cap)
+        assert info["merge_mode"] == 2
+        assert_same(lab, cnt, want_l, want_c, f"cap={cap}")
+    lab, cnt, info = gpu_fit(apd, x, 0.02, 8, max_edges=1 << 26)
+    assert info["merge_mode"] == 1
+    assert info["n_edges"] == (int(want_c.astype(np.int64).sum()) - 20000) // 2
+    assert_same(lab, cnt, want_l, want_c, "edges")
+
+
+def test_errors(apd):
+    import torch
+    x = datagen.uniform_points(1000, 3, 1)
+    bad = x.copy()
+    bad[500, 1] = np.nan
+    with pytest.raises(apd.DbscanError) as e:
+        gpu_fit(apd, bad, 0.1, 3)
+    assert e.value.status == -2
+    bad[500, 1] = np.inf
+    with pytest.raises(apd.DbscanError) as e:
+        gpu_fit(apd, bad, 0.1, 3)
+    assert e.value.status == -2
+    t = torch.from_numpy(x).cuda()
+    lab = torch.empty(1000, dtype=torch.int32, device="cuda")
+    need = apd.dbscan_workspace_bytes(1000, 3)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    st = apd.dbscan_fit_device(t.data_ptr(), 1000, 3, 0.1, 3, lab.data_ptr(),
+                               None, ws.data_ptr(), need - 256, None)
+    assert st == -5
+    st = apd.dbscan_fit_device(t.data_ptr(), 1000, 3, 0.1, 3, lab.data_ptr(),
+                               None, ws.data_ptr() + 16, need, None)
+    assert st == -5
+    st = apd.dbscan_fit_device(t.data_ptr(), 1000, 3, 0.1, 3, lab.data_ptr(),
+                               None, ws.data_ptr(), need, None)
+    assert st == 0
+    torch.cuda.synchronize()
+
+
+def test_host_entry_and_optional_counts(apd, orc):
+    import torch
+    x = datagen.gaussian_blobs(9000, 4, seed=9, n_blobs=3, sigma=0.04)
+    want_l, want_c, _ = orc.fit(x, 0.05, 6)
+    lab, cnt = apd.fit_host(x, 0.05, 6, return_counts=True)
+    assert_same(lab, cnt, want_l, want_c, "host entry")
+    lab = apd.fit(torch.from_numpy(x).cuda(), 0.05, 6).cpu().numpy()
+    assert np.array_equal(lab, want_l)
+    # n = 0 is a no-op
+    assert apd.fit_host(np.zeros((0, 3), np.float32), 0.1, 1).size == 0
+
+
+def test_repeatable(apd):
+    x, eps, m, _ = datagen.make_workload(2)
+    first = gpu_fit(apd, x, eps, m)
+    for _ in range(5):
+        again = gpu_fit(apd, x, eps, m)
+        assert np.array_equal(first[0], again[0])
+        assert np.array_equal(first[1], again[1])
+
+
+def _golden():
+    if not os.path.exists(GOLDEN_WORKLOADS):
+        return {}
+    with open(GOLDEN_WORKLOADS) as f:
+        return json.load(f)
+
+
+def _digest(a):
+    import hashlib
+    return hashlib.sha256(np.ascontiguousarray(a.astype("<i4")).tobytes()).hexdigest()
+
+
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+def test_named_workload(apd, orc, key):
+    x, eps, m, w = datagen.make_workload(key)
+    print(f"workload {key} {w.name}", flush=True)
+    lab, cnt, info = gpu_fit(apd, x, eps, m, max_edges=1 << 30)
+    assert info["merge_mode"] == 1
+    g = _golden().get(str(key))
+    if g is not None and g["points_sha256"] == datagen.sha256_points(x):
+        assert _digest(cnt) == g["counts_sha256"], "counts differ from the oracle"
+        assert _digest(lab) == g["labels_sha256"], "labels differ from the oracle"
+        assert int(info["n_core"]) == g["n_core"]
+    # rows recomputed by the oracle right now
+    rng = np.random.default_rng(key)
+    rows = rng.choice(w.n, size=min(w.n, 192), replace=False)
+    want = orc.row_counts(x, eps, rows)
+    assert np.array_equal(cnt[rows], want)
+    # invariants on sampled points, with core flags from the oracle: a core
+    # point shares its label with (a sample of) its core neighbours; a
+    # border point carries the label of its lowest-index core neighbour;
+    # noise has no core neighbour
+    for i in rng.choice(w.n, size=6, replace=False):
+        nb = orc.row_neighbours(x, eps, int(i))
+        assert nb.size == cnt[i]
+        if cnt[i] >= m:
+            some = rng.choice(nb, size=min(nb.size, 32), replace=False)
+            some_core = some[orc.row_counts(x, eps, some) >= m]
+            assert np.all(lab[some_core] == lab[i])
+        else:
+            lowest = None
+            for k in range(0, nb.size, 16):
+                part = nb[k:k + 16]
+                hit = part[orc.row_counts(x, eps, part) >= m]
+                if hit.size:
+                    lowest = int(hit.min())
+                    break
+            assert lab[i] == (-1 if lowest is None else lab[lowest])
+        if lab[i] != -1:
+            assert lab[i] <= i and lab[lab[i]] == lab[i]
+    if key <= 2:   # small enough for a live full oracle run
+        want_l, want_c, _ = orc.fit(x, eps, m)
+        assert_same(lab, cnt, want_l, want_c, w.name)
+
+
+@pytest.mark.parametrize("key", [1, 2, 3])
+def test_named_workload_tile_merge(apd, key):
+    x, eps, m, w = datagen.make_workload(key)
+    a = gpu_fit(apd, x, eps, m, max_edges=1 << 30)
+    b = gpu_fit(apd, x, eps, m, flags=2)
+    assert b[2]["merge_mode"] == 2 and b[2]["pass2_pairs"] > 0
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

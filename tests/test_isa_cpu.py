@@ -1,0 +1,63 @@
+"""Instruction checks on the gfx950 assembly of this library's own distance
+kernels (CPU only; hipcc cross-compiles).
+
+Bit-exact parity with the oracle needs every subtraction, square and
+addition of the distance rounded on its own: no fused or packed fp32
+multiply-add may appear in the count or tile-merge kernels.  The row
+points must arrive through scalar loads (wave-uniform operands), which is
+what keeps the inner loop at one VALU operation per arithmetic step.
+"""
+import re
+import shutil
+
+import pytest
+
+from all_pairs_distance_amd import build
+
+FORBIDDEN = re.compile(
+    r"\b(v_(fma|fmac|mad|mac)_f32|v_pk_(fma|mul|add)_f32|v_fma_mix\w*|"
+    r"v_mad_legacy_f32|v_fmac_legacy_f32|v_dot\w*)\b")
+
+
+def kernel_bodies(asm: str, marker: str):
+    out = {}
+    for m in re.finditer(r"^(_Z\S*" + marker + r"\S*):", asm, flags=re.M):
+        name = m.group(1)
+        end = asm.find("s_endpgm", m.end())
+        out[name] = asm[m.end():end]
+    return out
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if shutil.which(build.HIPCC) is None and not shutil.os.path.exists(build.HIPCC):
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("asm")
+    return {
+        "count": open(build.device_assembly(str(d / "c.s"), "k_count.hip")).read(),
+        "merge": open(build.device_assembly(str(d / "m.s"), "k_merge.hip")).read(),
+    }
+
+
+def test_count_kernels_have_no_fused_or_packed_fp32(asm):
+    bodies = kernel_bodies(asm["count"], "k_count")
+    assert len(bodies) == 24          # 12 widths x (edges, no edges)
+    for name, body in bodies.items():
+        bad = FORBIDDEN.findall(body)
+        assert not bad, (name, bad[:3])
+        assert "v_sub_f32" in body and "v_mul_f32" in body
+
+
+def test_tile_merge_kernels_have_no_fused_or_packed_fp32(asm):
+    bodies = kernel_bodies(asm["merge"], "k_merge_tiles")
+    assert len(bodies) == 12
+    for name, body in bodies.items():
+        assert not FORBIDDEN.findall(body), name
+
+
+def test_rows_are_scalar_loads(asm):
+    bodies = kernel_bodies(asm["count"], "k_countILi3ELb0")
+    (body,) = bodies.values()
+    assert re.search(r"s_load_dword", body)
+    # the distance takes its row operand straight from an SGPR
+    assert re.search(r"v_sub_f32_e32 v\d+, s\d+, v\d+", body)
