@@ -10,8 +10,9 @@ namespace dbk {
 // Point counts are padded to a multiple of this, so that every count-pass
 // variant (block sizes 256..4096 points) tiles the padded set exactly.
 constexpr int64_t kPadPoints = 4096;
-// Rows per work item of the tile passes (a multiple of the 64-lane wave).
-constexpr int kRowsPerItem = 256;
+// Rows per work item of the tile passes (a multiple of the 64-lane wave;
+// the count pass uses fewer when that would leave too few work items).
+constexpr int kRowsPerItem = 1024;
 // Edge records staged in LDS per wave before a flush to the edge area.
 constexpr int kEdgeStage = 256;
 constexpr int kThreads = 256;  // 4 waves of 64 lanes per workgroup

@@ -131,14 +131,22 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 #pragma unroll
       for (int k = 0; k < D; ++k) xr[k] = rp[k];
       unsigned acc = 0;
+      uint64_t m[P];
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const float s = dist2<D>(xr, xc[p]);
         const bool nb = s <= eps2;
-        const uint64_t m = ballot(nb);
-        acc += (unsigned)__popcll(m);
+        m[p] = ballot(nb);
+        acc += (unsigned)__popcll(m[p]);
         if (!DIAG) lc[p] += nb ? 1u : 0u;
-        if (EDGES) stage_edges<DIAG>(m, row, colw + p * 64, stage, fill, sink);
+      }
+      // the row's count over these columns is 0 for most rows: one
+      // wave-uniform branch per row keeps the P distance chains free of
+      // control flow so they interleave
+      if (EDGES && acc != 0) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+          stage_edges<DIAG>(m[p], row, colw + p * 64, stage, fill, sink);
       }
       rowv = write_lane(rowv, (int)acc, l);
     }
@@ -187,11 +195,15 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   const int64_t nb = L.n_pad / T;
-  const int rows = kRowsPerItem < T ? kRowsPerItem : T;
+  const int64_t tiles = nb * (nb + 1) / 2;
+  // rows per work item: up to kRowsPerItem, fewer (down to one wave's 64)
+  // while the launch would have under 4096 work-groups
+  int rows = kRowsPerItem < T ? kRowsPerItem : T;
+  while (rows > 64 && tiles * (T / rows) < 4096) rows >>= 1;
   const int chunks = T / rows;  // both powers of two
   int chunks_log2 = 0;
   while ((1 << chunks_log2) < chunks) ++chunks_log2;
-  const int64_t items = nb * (nb + 1) / 2 * chunks;
+  const int64_t items = tiles * chunks;
   const unsigned grid = (unsigned)(items < kMaxGrid ? items : kMaxGrid);
   if (edges)
     k_count<D, true><<<grid, kThreads, 0, s>>>(

@@ -48,7 +48,37 @@ def parse():
                     help="target length of the oracle sample run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB, "
+                         "so a counter run can scale FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
+
+
+COUNTER_PROFILE = os.path.join(ROOT, "profiles",
+                               "k_count_blobs_walks3d_n1000000_counters.md")
+COUNT_SOURCES = ["all_pairs_distance_amd/csrc/k_count.hip",
+                 "all_pairs_distance_amd/csrc/device.h",
+                 "all_pairs_distance_amd/csrc/internal.h"]
+
+
+def profiled_traffic(workload_name: str):
+    """HBM-side bytes per count-kernel launch from the committed counter
+    summary (scaled FETCH_SIZE + WRITE_SIZE), or None when that summary was
+    taken on another workload or on kernel sources that have changed since."""
+    if workload_name != "blobs_walks3d_n1000000" or not os.path.exists(COUNTER_PROFILE):
+        return None
+    fields = {}
+    for line in open(COUNTER_PROFILE):
+        if ":" in line and line.startswith("count-kernel-"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in COUNT_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if fields.get("count-kernel-sources-sha256") != h.hexdigest():
+        return None
+    return float(fields["count-kernel-traffic-bytes-per-launch"])
 
 
 def digest(a) -> str:
@@ -85,6 +115,13 @@ def main():
     x, eps, min_pts, w = datagen.make_workload(args.workload)
     n, d = x.shape
     dev = torch.device("cuda:0")
+    if args.calibrate_copy_mib:
+        src = torch.ones(args.calibrate_copy_mib << 18, dtype=torch.float32,
+                         device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     xt = torch.from_numpy(x).to(dev)
     ws = apd.Workspace(n, d, args.max_edges, device=dev)
     labels = torch.empty(n, dtype=torch.int32, device=dev)
@@ -168,7 +205,9 @@ def main():
             "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_TFLOPS,
-            "traffic": None,
+            "traffic": profiled_traffic(w.name),
+            "traffic_unit": "bytes per launch (HBM side, rocprofv3 FETCH_SIZE x2 "
+                            "+ WRITE_SIZE x1, scale from a 256 MiB copy)",
             "flops_per_launch": flops_count,
             "credit": "3d flops per ordered pair; each distance evaluated once "
                       "decides two ordered pairs",
