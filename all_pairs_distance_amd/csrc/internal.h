@@ -13,8 +13,9 @@ constexpr int64_t kPadPoints = 4096;
 // Rows per work item of the tile passes (a multiple of the 64-lane wave;
 // the count pass uses fewer when that would leave too few work items).
 constexpr int kRowsPerItem = 1024;
-// Edge records staged in LDS per wave before a flush to the edge area.
-constexpr int kEdgeStage = 256;
+// Edge records staged in LDS per wave before a flush to the edge area; at
+// least the 512 pairs of the (up to) 8 column groups staged per check.
+constexpr int kEdgeStage = 512;
 constexpr int kThreads = 256;  // 4 waves of 64 lanes per workgroup
 constexpr int kMaxGrid = 1 << 20;
 

@@ -30,6 +30,13 @@ constexpr int lane_points(int D) {
   return D <= 2 ? 16 : D <= 4 ? 8 : D <= 8 ? 4 : D <= 16 ? 2 : 1;
 }
 
+// Minimum waves per SIMD the register allocator is asked to allow (1 = no
+// constraint), chosen per width by measurement: the narrow widths fit 8
+// waves (<= 64 VGPRs) and run faster there; the wide ones would spill.
+constexpr int count_waves(int D, bool edges) {
+  return D <= 16 ? 8 : 1;
+}
+
 // Upper-triangle tile t (row-major over I <= J of nb x nb blocks) -> (I, J).
 __device__ __forceinline__ void tile_coords(int64_t t, int64_t nb, int64_t& I,
                                             int64_t& J) {
@@ -59,8 +66,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Copy the wave's staged edges to the edge area (one atomic per flush).
 // Slots past the capacity are dropped; the host sees the overflow because
 // the counter then exceeds the capacity.
-__device__ __noinline__ void flush_edges(uint2* stage, unsigned fill,
-                                         const EdgeSink& sink) {
+__device__ __forceinline__ void flush_edges(uint2* stage, unsigned fill,
+                                            const EdgeSink& sink) {
   wave_lds_sync();
   unsigned long long base = 0;
   if (lane_id() == 0) base = atomicAdd(sink.counter, (unsigned long long)fill);
@@ -73,28 +80,21 @@ __device__ __noinline__ void flush_edges(uint2* stage, unsigned fill,
 }
 
 // Stage the pairs (row, col0 + lane) of mask m; on a diagonal tile only the
-// pairs with col > row (each unordered pair once, never (i,i)).
+// pairs with col > row (each unordered pair once, never (i,i)).  The caller
+// has made room for every set bit.
 template <bool DIAG>
 __device__ __forceinline__ void stage_edges(uint64_t m, int64_t row,
-                                            int64_t col0, uint2* stage,
-                                            unsigned& fill,
-                                            const EdgeSink& sink) {
+                                            int64_t col0, int lane_col,
+                                            uint2* stage, unsigned& fill) {
   if (DIAG) {
     const int64_t first = row - col0 + 1;
     if (first >= 64) return;
     if (first > 0) m &= ~0ull << first;
   }
   if (m == 0) return;
-  const unsigned cnt = (unsigned)__popcll(m);
-  if (fill + cnt > (unsigned)kEdgeStage) {
-    flush_edges(stage, fill, sink);
-    fill = 0;
-  }
-  const int lane = lane_id();
-  if ((m >> lane) & 1ull)
-    stage[fill + bits_below(m)] =
-        make_uint2((unsigned)row, (unsigned)(col0 + lane));
-  fill += cnt;
+  if ((m >> lane_id()) & 1ull)
+    stage[fill + bits_below(m)] = make_uint2((unsigned)row, (unsigned)lane_col);
+  fill += (unsigned)__popcll(m);
 }
 
 // One work item: `rows` consecutive row points against this wave's 64*P
@@ -121,7 +121,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 
   for (int rb = 0; rb < rows; rb += 64) {
     int rowv = 0;  // lane l: count of row rb+l over these columns
-#pragma unroll 2
+#pragma unroll 1
     for (int l = 0; l < 64; ++l) {
       const int64_t row = row0 + rb + l;
       // wave-uniform address: read through the constant address space so
@@ -138,15 +138,31 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
         const bool nb = s <= eps2;
         m[p] = ballot(nb);
         acc += (unsigned)__popcll(m[p]);
-        if (!DIAG) lc[p] += nb ? 1u : 0u;
+        if (!DIAG) lc[p] = add_lane_bit(lc[p], m[p]);
       }
       // the row's count over these columns is 0 for most rows: one
       // wave-uniform branch per row keeps the P distance chains free of
       // control flow so they interleave
       if (EDGES && acc != 0) {
+        int lane_col = (int)(colw + lane);
+        // recomputed here, on the rare path, instead of P live registers
+        asm volatile("" : "+v"(lane_col));
+        // at most 8 column groups (512 pairs) are staged per capacity check
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-          stage_edges<DIAG>(m[p], row, colw + p * 64, stage, fill, sink);
+        for (int g = 0; g < P; g += 8) {
+          constexpr int G = P < 8 ? P : 8;
+          unsigned want = 0;
+#pragma unroll
+          for (int p = g; p < g + G; ++p) want += (unsigned)__popcll(m[p]);
+          if (fill + want > (unsigned)kEdgeStage) {
+            flush_edges(stage, fill, sink);
+            fill = 0;
+          }
+#pragma unroll
+          for (int p = g; p < g + G; ++p)
+            stage_edges<DIAG>(m[p], row, colw + p * 64, lane_col + p * 64,
+                              stage, fill);
+        }
       }
       rowv = write_lane(rowv, (int)acc, l);
     }
@@ -160,7 +176,8 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 }
 
 template <int D, bool EDGES>
-__global__ __launch_bounds__(kThreads) void k_count(
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES), 8))) void k_count(
     const float* __restrict__ pts, int64_t nb, int chunks_log2, int rows,
     int64_t items, float eps2, unsigned* __restrict__ count,
     uint2* __restrict__ edges, unsigned long long cap,
