@@ -48,6 +48,9 @@ def parse():
                     help="target length of the oracle sample run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--host-entry", action="store_true",
+                    help="also time dbscan_fit on host arrays (copies in and "
+                         "out included); reported apart, never as value")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, "
                          "so a counter run can scale FETCH_SIZE/WRITE_SIZE")
@@ -214,6 +217,19 @@ def main():
             "frac_distinct_pairs": achieved / 2 * (n - 1) / n / PEAK_FP32_TFLOPS,
         },
     }
+    if args.host_entry:
+        apd.fit_host(x, eps, min_pts)            # warm-up (allocations)
+        t0 = time.perf_counter()
+        lab_h = apd.fit_host(x, eps, min_pts)
+        t_h = time.perf_counter() - t0
+        out["pcie_inclusive"] = {
+            "value": pairs / t_h, "unit": "pair evaluations/s",
+            "ms": t_h * 1e3,
+            "what": "dbscan_fit on host arrays: device allocation, copies "
+                    "in and out, fit, frees",
+            "labels_match_device_entry": bool(
+                np.array_equal(lab_h, labels.cpu().numpy())),
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, eps, min_pts, args.cpu_seconds)
     print(json.dumps(out), flush=True)
