@@ -187,45 +187,50 @@ hipError_t launch_compact(const Layout& L, hipStream_t s) {
 }
 
 // ---- labels ----------------------------------------------------------------
-// Every core point finds its root (the smallest core of its component); a
-// border point takes the root of its lowest-index core neighbour.  Each
-// root collects the smallest member index with atomicMin; that index is
-// the cluster's label.  Roots are kept in bmin[] (unused for cores until
-// now) so the label pass needs no further pointer chasing.
+// Every core point finds its root, which is the smallest core of its
+// component (a root is only ever hung under a smaller root).  A border
+// point takes the root of its lowest-index core neighbour.  A cluster's
+// label is its smallest member: the root itself, unless a border point
+// with a smaller index joined it; only such border points touch cmin[]
+// (atomicMin), so no atomic is spent on cores.  Roots are kept in bmin[]
+// (unused for cores until now) for the label pass.
 __global__ void k_finalize(int64_t n, const unsigned char* __restrict__ core,
                            int* __restrict__ parent, int* __restrict__ bmin,
                            int* __restrict__ cmin) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
-    int r;
     if (core[i]) {
-      r = uf_find(parent, (int)i);
+      bmin[i] = uf_find(parent, (int)i);
     } else {
       const int b = bmin[i];
       if (b == INT_MAX) continue;
-      r = uf_find(parent, b);
+      const int r = uf_find(parent, b);
+      bmin[i] = r;
+      if (i < r) atomicMin(cmin + r, (int)i);
     }
-    bmin[i] = r;
-    atomicMin(cmin + r, (int)i);
   }
 }
 
-__global__ void k_write_labels(int64_t n, const unsigned char* __restrict__ core,
-                               const int* __restrict__ bmin,
+__global__ void k_write_labels(int64_t n, const int* __restrict__ bmin,
                                const int* __restrict__ cmin,
                                int* __restrict__ labels) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int r = bmin[i];
-    labels[i] = r == INT_MAX ? -1 : cmin[r];
+    if (r == INT_MAX) {
+      labels[i] = -1;
+    } else {
+      const int c = cmin[r];
+      labels[i] = c < r ? c : r;
+    }
   }
 }
 
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s) {
   k_finalize<<<grid_for(L.n, 256 * 4), 256, 0, s>>>(L.n, L.core, L.parent,
                                                     L.bmin, L.cmin);
-  k_write_labels<<<grid_for(L.n, 256 * 4), 256, 0, s>>>(L.n, L.core, L.bmin,
-                                                        L.cmin, labels);
+  k_write_labels<<<grid_for(L.n, 256 * 4), 256, 0, s>>>(L.n, L.bmin, L.cmin,
+                                                        labels);
   return hipGetLastError();
 }
 
