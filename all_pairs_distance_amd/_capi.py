@@ -23,6 +23,7 @@ ERR_HIP = -6
 MERGE_NONE, MERGE_EDGES, MERGE_TILES = 0, 1, 2
 FLAG_TIME_PHASES = 0x1
 FLAG_FORCE_TILE_MERGE = 0x2
+FLAG_PRUNE_TILES = 0x4
 MAX_D = 64
 
 
@@ -33,6 +34,8 @@ class dbscan_info(ctypes.Structure):
         ("edge_capacity", ctypes.c_int64),
         ("pass1_pairs", ctypes.c_int64),
         ("pass2_pairs", ctypes.c_int64),
+        ("tiles_total", ctypes.c_int64),
+        ("tiles_kept", ctypes.c_int64),
         ("merge_mode", ctypes.c_int32),
         ("timed", ctypes.c_int32),
         ("ms_layout", ctypes.c_float),

@@ -23,7 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdbscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "k_count.hip", "k_prep.hip", "k_merge.hip"]
+SOURCES = ["api.hip", "k_count.hip", "k_prep.hip", "k_merge.hip",
+           "k_prune.hip"]
 HEADERS = ["internal.h", "device.h"]
 ARCH = "gfx950"
 FLAGS = [

@@ -21,10 +21,27 @@ static int64_t pad_points(int64_t n) {
   return (n + kPadPoints - 1) / kPadPoints * kPadPoints;
 }
 
+static size_t sort_bytes(int64_t n_pad) {
+  size_t b = prune_sort_bytes(n_pad);
+  // the size query needs a device; without one, a generous estimate
+  if (b == 0) b = (size_t)n_pad * 16 + ((size_t)1 << 20);
+  return b;
+}
+
+static int64_t tile_capacity(int64_t n_pad, int D) {
+  const int64_t nb = n_pad / block_points(D);
+  const int64_t all = nb * (nb + 1) / 2;
+  return all < kTileListCap ? all : kTileListCap;
+}
+
+constexpr int kRegions = 19;
+
 // Region sizes in carve order; every region starts 256-byte aligned.
-static size_t regions(int64_t n_pad, int S, size_t* out) {
+static size_t regions(int64_t n_pad, int D, size_t* out) {
   const size_t np = (size_t)n_pad;
-  size_t sz[] = {
+  const size_t S = (size_t)row_stride(D);
+  const size_t nb = np / (size_t)block_points(D);
+  size_t sz[kRegions] = {
       sizeof(Status),                // status
       np * S * sizeof(float),        // pts
       np * sizeof(unsigned),         // count
@@ -35,9 +52,18 @@ static size_t regions(int64_t n_pad, int S, size_t* out) {
       np * sizeof(int),              // core_list
       np * S * sizeof(float),        // core_pts
       (np / 1024 + 1) * sizeof(unsigned),  // block_sums
+      6 * sizeof(unsigned),          // bbox
+      np * sizeof(unsigned),         // keys_in
+      np * sizeof(unsigned),         // keys_out
+      np * sizeof(int),              // idx_in
+      np * sizeof(int),              // perm
+      np * S * sizeof(float),        // sorted_pts
+      nb * 2 * S * sizeof(float),    // boxes
+      (size_t)tile_capacity(n_pad, D) * sizeof(uint2),  // tiles
+      sort_bytes(n_pad),             // radix sort scratch
   };
   size_t total = 0;
-  for (int r = 0; r < 10; ++r) {
+  for (int r = 0; r < kRegions; ++r) {
     if (out) out[r] = total;
     total += align_up(sz[r], 256);
   }
@@ -47,12 +73,12 @@ static size_t regions(int64_t n_pad, int S, size_t* out) {
 size_t layout_min_bytes(int64_t n, int d) {
   const int D = pick_dim(d);
   if (n < 0 || n > INT32_MAX || D == 0) return 0;
-  return regions(pad_points(n < 1 ? 1 : n), row_stride(D), nullptr);
+  return regions(pad_points(n < 1 ? 1 : n), D, nullptr);
 }
 
 bool carve(Layout& L, void* ws, size_t ws_bytes) {
-  size_t off[10];
-  const size_t need = regions(L.n_pad, L.stride, off);
+  size_t off[kRegions];
+  const size_t need = regions(L.n_pad, L.D, off);
   if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 255u)) return false;
   char* b = static_cast<char*>(ws);
   L.status = reinterpret_cast<Status*>(b + off[0]);
@@ -65,6 +91,17 @@ bool carve(Layout& L, void* ws, size_t ws_bytes) {
   L.core_list = reinterpret_cast<int*>(b + off[7]);
   L.core_pts = reinterpret_cast<float*>(b + off[8]);
   L.block_sums = reinterpret_cast<unsigned*>(b + off[9]);
+  L.bbox = reinterpret_cast<unsigned*>(b + off[10]);
+  L.keys_in = reinterpret_cast<unsigned*>(b + off[11]);
+  L.keys_out = reinterpret_cast<unsigned*>(b + off[12]);
+  L.idx_in = reinterpret_cast<int*>(b + off[13]);
+  L.perm = reinterpret_cast<int*>(b + off[14]);
+  L.sorted_pts = reinterpret_cast<float*>(b + off[15]);
+  L.boxes = reinterpret_cast<float*>(b + off[16]);
+  L.tiles = reinterpret_cast<uint2*>(b + off[17]);
+  L.tile_cap = (unsigned long long)tile_capacity(L.n_pad, L.D);
+  L.sort_tmp = b + off[18];
+  L.sort_tmp_bytes = need - off[18];
   L.bytes_min = need;
   const size_t spare = ws_bytes - need;
   L.edges = reinterpret_cast<uint2*>(b + need);
@@ -79,8 +116,9 @@ using namespace dbk;
 
 namespace {
 
-constexpr uint32_t kKnownFlags =
-    DBSCAN_FLAG_TIME_PHASES | DBSCAN_FLAG_FORCE_TILE_MERGE;
+constexpr uint32_t kKnownFlags = DBSCAN_FLAG_TIME_PHASES |
+                                  DBSCAN_FLAG_FORCE_TILE_MERGE |
+                                  DBSCAN_FLAG_PRUNE_TILES;
 
 int check_args(int64_t n, int32_t d, float eps, int32_t min_pts) {
   if (n < 0 || n > (int64_t)INT32_MAX) return DBSCAN_ERR_INVALID_ARG;
@@ -204,13 +242,15 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   const float eps2 = eps_v * eps_v;
   const bool want_edges =
       L.edge_cap > 0 && !(flags & DBSCAN_FLAG_FORCE_TILE_MERGE);
+  const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
   int64_t pass1 = 0, pass2 = 0;
 
   tm.mark(0);
   DB_TRY(launch_prepare(L, d_points, stream));
+  if (prune) DB_TRY(launch_prune(L, block_points(L.D), eps2, stream));
   tm.mark(1);
-  DB_TRY(launch_count(L, eps2, want_edges, stream, &pass1));
+  DB_TRY(launch_count(L, eps2, want_edges, prune, stream, &pass1));
   tm.mark(2);
   DB_TRY(launch_core(L, min_pts, d_counts, stream));
 
@@ -247,6 +287,11 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
     info->n_core = n_core;
     info->n_edges = want_edges ? (int64_t)host_st.n_edges : 0;
     info->edge_capacity = (int64_t)L.edge_cap;
+    const int64_t nb = L.n_pad / block_points(L.D);
+    info->tiles_total = nb * (nb + 1) / 2;
+    info->tiles_kept = prune && host_st.n_tiles <= L.tile_cap
+                           ? (int64_t)host_st.n_tiles
+                           : info->tiles_total;
     info->pass1_pairs = pass1;
     info->pass2_pairs = pass2;
     info->merge_mode = mode;

@@ -28,6 +28,7 @@ __device__ __forceinline__ float dist2(const float* a, const float* b) {
 // Read-only global memory seen through the constant address space: loads
 // from wave-uniform addresses through such a pointer become scalar loads.
 typedef const float __attribute__((address_space(4)))* const_float_ptr;
+typedef const int __attribute__((address_space(4)))* const_int_ptr;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

@@ -25,7 +25,9 @@ struct Status {
   unsigned int n_core;             // number of core points
   unsigned long long n_edges;      // edge slots reserved by the count pass
   unsigned int n_core_list;        // entries written by the core compaction
-  unsigned int pad[11];
+  unsigned int pad0;
+  unsigned long long n_tiles;      // block pairs kept by the tile pruning
+  unsigned int pad[8];
 };
 static_assert(sizeof(Status) == 64, "status block is 64 bytes");
 
@@ -38,6 +40,15 @@ constexpr int row_stride(int D) { return D <= 2 ? D : ((D + 3) & ~3); }
 // (extra coordinates are 0 on both sides, which adds exact zeros to the sum).
 constexpr int kDims[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
 int pick_dim(int d);  // smallest compiled D >= d, or 0
+
+// Column points per lane of the count pass (P) for width D; its blocks hold
+// T = 256 * P points (4 waves of 64 lanes).
+constexpr int lane_points(int D) {
+  return D <= 2 ? 16 : D <= 4 ? 8 : D <= 8 ? 4 : D <= 16 ? 2 : 1;
+}
+constexpr int block_points(int D) { return 256 * lane_points(D); }
+// Most block pairs a pruning tile list holds (beyond: no pruning).
+constexpr int64_t kTileListCap = (int64_t)1 << 24;
 
 struct Layout {
   int64_t n, n_pad;
@@ -53,6 +64,18 @@ struct Layout {
   int* core_list;      // [n_pad] compacted core indices (tile merge)
   float* core_pts;     // [n_pad][stride] their coordinates (tile merge)
   unsigned* block_sums;// [n_pad / 1024 + 1] compaction scan
+  // tile pruning (used only when asked for)
+  unsigned* bbox;      // [6] order-encoded min/max of 3 coordinates
+  unsigned* keys_in;   // [n_pad] sort keys
+  unsigned* keys_out;  // [n_pad]
+  int* idx_in;         // [n_pad] 0..n_pad-1
+  int* perm;           // [n_pad] sorted position -> original index
+  float* sorted_pts;   // [n_pad][stride] points in sorted order
+  float* boxes;        // [nb][2][stride] block bounding boxes
+  uint2* tiles;        // kept block pairs
+  unsigned long long tile_cap;
+  void* sort_tmp;      // radix sort scratch
+  size_t sort_tmp_bytes;
   uint2* edges;        // edge area (may be empty)
   unsigned long long edge_cap;
   size_t bytes_min;    // minimum workspace
@@ -63,8 +86,10 @@ bool carve(Layout& L, void* ws, size_t ws_bytes);
 
 // ---- launchers (each enqueues on `s` and returns hipGetLastError) -------
 hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s);
-hipError_t launch_count(const Layout& L, float eps2, bool edges, hipStream_t s,
-                        int64_t* pairs);
+hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
+                        hipStream_t s, int64_t* pairs);
+size_t prune_sort_bytes(int64_t n_pad);
+hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s);
 hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
                        hipStream_t s);
 hipError_t launch_compact(const Layout& L, hipStream_t s);

@@ -25,11 +25,6 @@
 
 namespace dbk {
 
-// Column points per lane: P*D coordinates + P counters stay in VGPRs.
-constexpr int lane_points(int D) {
-  return D <= 2 ? 16 : D <= 4 ? 8 : D <= 8 ? 4 : D <= 16 ? 2 : 1;
-}
-
 // Minimum waves per SIMD the register allocator is asked to allow (1 = no
 // constraint), chosen per width by measurement: the narrow widths fit 8
 // waves (<= 64 VGPRs) and run faster there; the wide ones would spill.
@@ -79,13 +74,15 @@ __device__ __forceinline__ void flush_edges(uint2* stage, unsigned fill,
   wave_lds_sync();
 }
 
-// Stage the pairs (row, col0 + lane) of mask m; on a diagonal tile only the
-// pairs with col > row (each unordered pair once, never (i,i)).  The caller
-// has made room for every set bit.
+// Stage the pairs (row_out, col_out) of mask m, where row and col0 + lane
+// are the positions in the tile; on a diagonal tile only the pairs with
+// col > row (each unordered pair once, never (i,i)).  The caller has made
+// room for every set bit.
 template <bool DIAG>
 __device__ __forceinline__ void stage_edges(uint64_t m, int64_t row,
-                                            int64_t col0, int lane_col,
-                                            uint2* stage, unsigned& fill) {
+                                            int64_t col0, int row_out,
+                                            int col_out, uint2* stage,
+                                            unsigned& fill) {
   if (DIAG) {
     const int64_t first = row - col0 + 1;
     if (first >= 64) return;
@@ -93,19 +90,22 @@ __device__ __forceinline__ void stage_edges(uint64_t m, int64_t row,
   }
   if (m == 0) return;
   if ((m >> lane_id()) & 1ull)
-    stage[fill + bits_below(m)] = make_uint2((unsigned)row, (unsigned)lane_col);
+    stage[fill + bits_below(m)] = make_uint2((unsigned)row_out, (unsigned)col_out);
   fill += (unsigned)__popcll(m);
 }
 
 // One work item: `rows` consecutive row points against this wave's 64*P
 // column points.
-template <int D, int P, bool DIAG, bool EDGES>
+// With PRUNED, pts is the sorted copy and perm maps a sorted position to
+// the original index: counts and captured pairs go to original indices.
+template <int D, int P, bool DIAG, bool EDGES, bool PRUNED>
 __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            int64_t row0, int rows,
                                            int64_t colw, float eps2,
                                            unsigned* __restrict__ count,
                                            uint2* stage, unsigned& fill,
-                                           const EdgeSink& sink) {
+                                           const EdgeSink& sink,
+                                           const int* __restrict__ perm) {
   constexpr int S = row_stride(D);
   const int lane = lane_id();
   float xc[P][D];
@@ -147,6 +147,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
         int lane_col = (int)(colw + lane);
         // recomputed here, on the rare path, instead of P live registers
         asm volatile("" : "+v"(lane_col));
+        const int row_out = PRUNED ? ((const_int_ptr)perm)[row] : (int)row;
         // at most 8 column groups (512 pairs) are staged per capacity check
 #pragma unroll
         for (int g = 0; g < P; g += 8) {
@@ -159,29 +160,39 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
             fill = 0;
           }
 #pragma unroll
-          for (int p = g; p < g + G; ++p)
-            stage_edges<DIAG>(m[p], row, colw + p * 64, lane_col + p * 64,
-                              stage, fill);
+          for (int p = g; p < g + G; ++p) {
+            const int col = lane_col + p * 64;
+            stage_edges<DIAG>(m[p], row, colw + p * 64, row_out,
+                              PRUNED ? perm[col] : col, stage, fill);
+          }
         }
       }
       rowv = write_lane(rowv, (int)acc, l);
     }
-    if (rowv) atomicAdd(count + row0 + rb + lane, (unsigned)rowv);
+    if (rowv) {
+      const int64_t r = row0 + rb + lane;
+      atomicAdd(count + (PRUNED ? perm[r] : r), (unsigned)rowv);
+    }
   }
   if (!DIAG) {
 #pragma unroll
     for (int p = 0; p < P; ++p)
-      if (lc[p]) atomicAdd(count + colw + p * 64 + lane, lc[p]);
+      if (lc[p]) {
+        const int64_t c = colw + p * 64 + lane;
+        atomicAdd(count + (PRUNED ? perm[c] : c), lc[p]);
+      }
   }
 }
 
-template <int D, bool EDGES>
+template <int D, bool EDGES, bool PRUNED>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES), 8))) void k_count(
     const float* __restrict__ pts, int64_t nb, int chunks_log2, int rows,
     int64_t items, float eps2, unsigned* __restrict__ count,
     uint2* __restrict__ edges, unsigned long long cap,
-    unsigned long long* __restrict__ counter) {
+    unsigned long long* __restrict__ counter,
+    const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
+    unsigned long long tile_cap, const int* __restrict__ perm) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
@@ -189,66 +200,85 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES), 8))) void k_count(
   uint2* stage = stage_all + (EDGES ? wave * kEdgeStage : 0);
   unsigned fill = 0;
   const EdgeSink sink{edges, cap, counter};
+  // pruned: walk the kept block pairs (written by the previous kernel);
+  // if the list overflowed, every block pair of the sorted points
+  bool from_list = false;
+  if (PRUNED) {
+    const unsigned long long kept = *n_tiles;
+    if (kept <= tile_cap) {
+      items = (int64_t)kept << chunks_log2;
+      from_list = true;
+    }
+  }
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int64_t tile = item >> chunks_log2;
     const int c = (int)(item & ((1 << chunks_log2) - 1));
     int64_t I, J;
-    tile_coords(tile, nb, I, J);
+    if (PRUNED && from_list) {
+      const uint2 tl = tiles[tile];
+      I = tl.x;
+      J = tl.y;
+    } else {
+      tile_coords(tile, nb, I, J);
+    }
     const int64_t row0 = I * T + (int64_t)c * rows;
     const int64_t colw = J * T + (int64_t)wave * 64 * P;
     if (I == J)
-      count_item<D, P, true, EDGES>(pts, row0, rows, colw, eps2, count, stage,
-                                    fill, sink);
+      count_item<D, P, true, EDGES, PRUNED>(pts, row0, rows, colw, eps2, count,
+                                            stage, fill, sink, perm);
     else
-      count_item<D, P, false, EDGES>(pts, row0, rows, colw, eps2, count,
-                                     stage, fill, sink);
+      count_item<D, P, false, EDGES, PRUNED>(pts, row0, rows, colw, eps2,
+                                             count, stage, fill, sink, perm);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
 
 template <int D>
 static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
-                                 hipStream_t s, int64_t* pairs) {
+                                 bool pruned, hipStream_t s, int64_t* pairs) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   const int64_t nb = L.n_pad / T;
   const int64_t tiles = nb * (nb + 1) / 2;
   // rows per work item: up to kRowsPerItem, fewer (down to one wave's 64)
-  // while the launch would have under 4096 work-groups
+  // while the full triangle would give under 4096 work items (a pruned
+  // launch keeps some of them; how many is only known on the device)
   int rows = kRowsPerItem < T ? kRowsPerItem : T;
   while (rows > 64 && tiles * (T / rows) < 4096) rows >>= 1;
   const int chunks = T / rows;  // both powers of two
   int chunks_log2 = 0;
   while ((1 << chunks_log2) < chunks) ++chunks_log2;
   const int64_t items = tiles * chunks;
-  const unsigned grid = (unsigned)(items < kMaxGrid ? items : kMaxGrid);
-  if (edges)
-    k_count<D, true><<<grid, kThreads, 0, s>>>(
-        L.pts, nb, chunks_log2, rows, items, eps2, L.count, L.edges, L.edge_cap,
-        &L.status->n_edges);
+  const int64_t max_grid = pruned ? 16384 : kMaxGrid;
+  const unsigned grid = (unsigned)(items < max_grid ? items : max_grid);
+  const float* pts = pruned ? L.sorted_pts : L.pts;
+  const unsigned long long* n_tiles = &L.status->n_tiles;
+#define DBK_COUNT_ARGS                                                      \
+  pts, nb, chunks_log2, rows, items, eps2, L.count,                         \
+      edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
+      &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm
+  if (edges && pruned)
+    k_count<D, true, true><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
+  else if (edges)
+    k_count<D, true, false><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
+  else if (pruned)
+    k_count<D, false, true><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
   else
-    k_count<D, false><<<grid, kThreads, 0, s>>>(
-        L.pts, nb, chunks_log2, rows, items, eps2, L.count, nullptr, 0ull,
-        &L.status->n_edges);
+    k_count<D, false, false><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
+#undef DBK_COUNT_ARGS
   if (pairs) *pairs = L.n_pad * L.n_pad;
   return hipGetLastError();
 }
 
-hipError_t launch_count(const Layout& L, float eps2, bool edges, hipStream_t s,
-                        int64_t* pairs) {
+hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
+                        hipStream_t s, int64_t* pairs) {
   switch (L.D) {
-    case 1: return launch_count_d<1>(L, eps2, edges, s, pairs);
-    case 2: return launch_count_d<2>(L, eps2, edges, s, pairs);
-    case 3: return launch_count_d<3>(L, eps2, edges, s, pairs);
-    case 4: return launch_count_d<4>(L, eps2, edges, s, pairs);
-    case 6: return launch_count_d<6>(L, eps2, edges, s, pairs);
-    case 8: return launch_count_d<8>(L, eps2, edges, s, pairs);
-    case 12: return launch_count_d<12>(L, eps2, edges, s, pairs);
-    case 16: return launch_count_d<16>(L, eps2, edges, s, pairs);
-    case 24: return launch_count_d<24>(L, eps2, edges, s, pairs);
-    case 32: return launch_count_d<32>(L, eps2, edges, s, pairs);
-    case 48: return launch_count_d<48>(L, eps2, edges, s, pairs);
-    case 64: return launch_count_d<64>(L, eps2, edges, s, pairs);
+#define DBK_CASE(DD) \
+  case DD: return launch_count_d<DD>(L, eps2, edges, pruned, s, pairs);
+    DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
+    DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)
+    DBK_CASE(64)
+#undef DBK_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -55,10 +55,6 @@ hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
   return hipGetLastError();
 }
 
-constexpr int merge_lane_points(int D) {
-  return D <= 2 ? 16 : D <= 4 ? 8 : D <= 8 ? 4 : D <= 16 ? 2 : 1;
-}
-
 typedef const unsigned char __attribute__((address_space(4)))* const_u8_ptr;
 
 template <int D>
@@ -67,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     const int* __restrict__ core_list, const unsigned char* __restrict__ core,
     int64_t row_blocks, int64_t col_blocks, float eps2, int* parent,
     int* __restrict__ bmin) {
-  constexpr int P = merge_lane_points(D);
+  constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
   const int lane = lane_id();
@@ -119,7 +115,7 @@ template <int D>
 static hipError_t launch_merge_tiles_d(const Layout& L, float eps2,
                                        int64_t n_core, hipStream_t s,
                                        int64_t* pairs) {
-  constexpr int T = 256 * merge_lane_points(D);
+  constexpr int T = 256 * lane_points(D);
   const int64_t nc_pad = (n_core + T - 1) / T * T;
   const int64_t col_blocks = nc_pad / T;
   const int64_t row_blocks = L.n_pad / kRowsPerItem;

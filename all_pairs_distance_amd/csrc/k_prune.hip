@@ -1,0 +1,255 @@
+// Exact tile pruning for the neighbour-count pass (an opt-in mode).
+//
+// The points are put in a locality-preserving order (a Morton key over the
+// first min(d,3) coordinates, sorted), each block of T consecutive sorted
+// points gets its bounding box, and a block pair (I, J) is skipped when the
+// boxes are provably farther apart than eps in the same fp32 arithmetic the
+// distance uses:
+//   G_k = fl(lo_J,k - hi_I,k) (or the mirror) when the boxes are apart in
+//   dimension k, else 0; Gs = (((fl(G_0^2) + fl(G_1^2)) + fl(G_2^2)) ...)
+//   summed in ascending k with every step rounded.
+// For x in block I and y in block J, |x_k - y_k| >= the real gap, rounding
+// is monotone, so |fl(x_k - y_k)| >= G_k, fl(t^2) >= fl(G_k^2), and each
+// rounded partial sum of the true distance is >= the matching partial sum
+// of Gs.  Gs > eps2 therefore implies d2(x,y) > eps2 for every pair of the
+// two blocks: no neighbour is ever skipped, and counts, captured pairs and
+// labels stay bit-identical to the unpruned pass.
+//
+// This follows the domain partitioning of CUDAScan as described by Wang et
+// al., Sec. III (blocks of nearby points handled together), restated as a
+// pruning rule on the all-pairs tiles.
+#include <climits>
+
+#include <rocprim/device/device_radix_sort.hpp>
+
+#include "device.h"
+#include "internal.h"
+
+namespace dbk {
+
+static unsigned grid_for_p(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (unsigned)(g < kMaxGrid ? g : kMaxGrid);
+}
+
+// float <-> order-preserving unsigned
+__device__ __forceinline__ unsigned ord_u(float f) {
+  unsigned b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float ord_f(unsigned u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Global min/max of the first KD coordinates of the real points.
+__global__ void k_bbox(const float* __restrict__ pts, int64_t n, int S, int KD,
+                       unsigned* __restrict__ lohi) {
+  unsigned lo[3] = {~0u, ~0u, ~0u}, hi[3] = {0u, 0u, 0u};
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    for (int k = 0; k < KD; ++k) {
+      const unsigned u = ord_u(pts[i * S + k]);
+      lo[k] = u < lo[k] ? u : lo[k];
+      hi[k] = u > hi[k] ? u : hi[k];
+    }
+  }
+  for (int k = 0; k < KD; ++k) {
+    unsigned a = lo[k], b = hi[k];
+    for (int off = 32; off > 0; off >>= 1) {
+      const unsigned oa = __shfl_xor(a, off), ob = __shfl_xor(b, off);
+      a = oa < a ? oa : a;
+      b = ob > b ? ob : b;
+    }
+    if (lane_id() == 0) {
+      atomicMin(lohi + k, a);
+      atomicMax(lohi + 3 + k, b);
+    }
+  }
+}
+
+__global__ void k_bbox_init(unsigned* lohi) {
+  if (threadIdx.x < 3) lohi[threadIdx.x] = ~0u;
+  else if (threadIdx.x < 6) lohi[threadIdx.x] = 0u;
+}
+
+// Spread the low 10 bits of v to every third bit.
+__device__ __forceinline__ unsigned spread3(unsigned v) {
+  v &= 0x3ffu;
+  v = (v | (v << 16)) & 0x030000ffu;
+  v = (v | (v << 8)) & 0x0300f00fu;
+  v = (v | (v << 4)) & 0x030c30c3u;
+  v = (v | (v << 2)) & 0x09249249u;
+  return v;
+}
+// Spread the low 15 bits of v to every second bit.
+__device__ __forceinline__ unsigned spread2(unsigned v) {
+  v &= 0x7fffu;
+  v = (v | (v << 8)) & 0x00ff00ffu;
+  v = (v | (v << 4)) & 0x0f0f0f0fu;
+  v = (v | (v << 2)) & 0x33333333u;
+  v = (v | (v << 1)) & 0x55555555u;
+  return v;
+}
+
+// Sort keys: d = 1 sorts by the value itself; d = 2 and d >= 3 use a Morton
+// code of 15 / 10 bits per coordinate over the bounding box.  Padding rows
+// get the largest key (they sort last, after every real point).
+__global__ void k_keys(const float* __restrict__ pts, int64_t n, int64_t n_pad,
+                       int S, int KD, const unsigned* __restrict__ lohi,
+                       unsigned* __restrict__ keys, int* __restrict__ idx) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    unsigned key = 0xffffffffu;
+    if (i < n) {
+      if (KD == 1) {
+        key = ord_u(pts[i * S]) >> 1;  // order kept, below the padding key
+      } else {
+        const int bits = KD == 2 ? 15 : 10;
+        const float cells = (float)((1 << bits) - 1);
+        unsigned q[3] = {0, 0, 0};
+        for (int k = 0; k < KD; ++k) {
+          const float lo = ord_f(lohi[k]), hi = ord_f(lohi[3 + k]);
+          const float span = hi - lo;
+          float f = span > 0.f ? (pts[i * S + k] - lo) / span * cells : 0.f;
+          f = f < 0.f ? 0.f : (f > cells ? cells : f);
+          q[k] = (unsigned)f;
+        }
+        key = KD == 2 ? (spread2(q[0]) | (spread2(q[1]) << 1))
+                      : (spread3(q[0]) | (spread3(q[1]) << 1) |
+                         (spread3(q[2]) << 2));
+      }
+    }
+    keys[i] = key;
+    idx[i] = (int)i;
+  }
+}
+
+// sorted_pts[s] = pts[perm[s]]
+__global__ void k_gather(const float* __restrict__ pts,
+                         const int* __restrict__ perm, int64_t total, int S,
+                         float* __restrict__ out) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t s = e / S;
+    const int k = (int)(e - s * S);
+    out[e] = pts[(int64_t)perm[s] * S + k];
+  }
+}
+
+// Bounding box of each block of T sorted points over all S coordinates;
+// padding rows are skipped, an all-padding block gets lo > hi.
+__global__ __launch_bounds__(256) void k_block_boxes(
+    const float* __restrict__ spts, const int* __restrict__ perm, int64_t n,
+    int T, int S, float* __restrict__ boxes) {
+  const int64_t b = blockIdx.x;
+  for (int k = 0; k < S; ++k) {
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+    for (int t = threadIdx.x; t < T; t += 256) {
+      const int64_t s = b * T + t;
+      if (perm[s] < n) {
+        const float v = spts[s * S + k];
+        lo = v < lo ? v : lo;
+        hi = v > hi ? v : hi;
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ol = __shfl_xor(lo, off), oh = __shfl_xor(hi, off);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    __shared__ float sl[4], sh[4];
+    if (lane_id() == 0) {
+      sl[threadIdx.x >> 6] = lo;
+      sh[threadIdx.x >> 6] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float l = sl[0], h = sh[0];
+      for (int w = 1; w < 4; ++w) {
+        l = sl[w] < l ? sl[w] : l;
+        h = sh[w] > h ? sh[w] : h;
+      }
+      boxes[(b * 2) * S + k] = l;
+      boxes[(b * 2 + 1) * S + k] = h;
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void tile_coords_p(int64_t t, int64_t nb, int64_t& I,
+                                              int64_t& J) {
+  const double b = 2.0 * (double)nb + 1.0;
+  int64_t i = (int64_t)((b - sqrt(b * b - 8.0 * (double)t)) * 0.5);
+  if (i < 0) i = 0;
+  if (i > nb - 1) i = nb - 1;
+  while (i > 0 && i * nb - i * (i - 1) / 2 > t) --i;
+  while (i + 1 < nb && (i + 1) * nb - (i + 1) * i / 2 <= t) ++i;
+  I = i;
+  J = i + (t - (i * nb - i * (i - 1) / 2));
+}
+
+// Keep block pair (I, J), I <= J, unless the fp32 box-gap bound exceeds
+// eps2.  Kept pairs are appended to the list (any order).
+__global__ void k_tile_list(const float* __restrict__ boxes, int64_t nb, int S,
+                            float eps2, uint2* __restrict__ list,
+                            unsigned long long cap, Status* __restrict__ st) {
+  const int64_t tiles = nb * (nb + 1) / 2;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < tiles;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int64_t I, J;
+    tile_coords_p(t, nb, I, J);
+    const float* bi = boxes + I * 2 * S;
+    const float* bj = boxes + J * 2 * S;
+    bool keep = bi[0] <= bi[S] && bj[0] <= bj[S];  // both blocks hold points
+    if (keep && I != J) {
+      float s = 0.f;
+      for (int k = 0; k < S; ++k) {
+        const float loi = bi[k], hii = bi[S + k], loj = bj[k], hij = bj[S + k];
+        float g = 0.f;
+        if (loj > hii) g = loj - hii;
+        else if (loi > hij) g = loi - hij;
+        const float q = g * g;
+        s = k == 0 ? q : s + q;
+      }
+      keep = !(s > eps2);
+    }
+    if (keep) {
+      const unsigned long long slot = atomicAdd(&st->n_tiles, 1ull);
+      if (slot < cap) list[slot] = make_uint2((unsigned)I, (unsigned)J);
+    }
+  }
+}
+
+size_t prune_sort_bytes(int64_t n_pad) {
+  size_t bytes = 0;
+  (void)rocprim::radix_sort_pairs(nullptr, bytes, (unsigned*)nullptr,
+                                  (unsigned*)nullptr, (int*)nullptr,
+                                  (int*)nullptr, (size_t)n_pad, 0u, 32u);
+  return bytes;
+}
+
+hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s) {
+  const int KD = L.d < 3 ? L.d : 3;
+  k_bbox_init<<<1, 64, 0, s>>>(L.bbox);
+  k_bbox<<<grid_for_p(L.n, 256 * 16), 256, 0, s>>>(L.pts, L.n, L.stride, KD,
+                                                   L.bbox);
+  k_keys<<<grid_for_p(L.n_pad, 256 * 4), 256, 0, s>>>(
+      L.pts, L.n, L.n_pad, L.stride, KD, L.bbox, L.keys_in, L.idx_in);
+  size_t bytes = L.sort_tmp_bytes;
+  hipError_t e = rocprim::radix_sort_pairs(
+      L.sort_tmp, bytes, L.keys_in, L.keys_out, L.idx_in, L.perm,
+      (size_t)L.n_pad, 0u, 32u, s);
+  if (e != hipSuccess) return e;
+  k_gather<<<grid_for_p(L.n_pad * L.stride, 256 * 8), 256, 0, s>>>(
+      L.pts, L.perm, L.n_pad * L.stride, L.stride, L.sorted_pts);
+  const int64_t nb = L.n_pad / T;
+  k_block_boxes<<<(unsigned)nb, 256, 0, s>>>(L.sorted_pts, L.perm, L.n, T,
+                                             L.stride, L.boxes);
+  const int64_t tiles = nb * (nb + 1) / 2;
+  k_tile_list<<<grid_for_p(tiles, 256), 256, 0, s>>>(
+      L.boxes, nb, L.stride, eps2, L.tiles, L.tile_cap, L.status);
+  return hipGetLastError();
+}
+
+}  // namespace dbk

@@ -48,6 +48,10 @@ def parse():
                     help="target length of the oracle sample run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--prune", action="store_true",
+                    help="time the exact tile-pruned fit as the main line")
+    ap.add_argument("--no-pruned-line", action="store_true",
+                    help="skip the extra pruned_mode measurement")
     ap.add_argument("--host-entry", action="store_true",
                     help="also time dbscan_fit on host arrays (copies in and "
                          "out included); reported apart, never as value")
@@ -130,32 +134,36 @@ def main():
     labels = torch.empty(n, dtype=torch.int32, device=dev)
     counts = torch.empty(n, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    flags = apd.FLAG_TIME_PHASES | (apd.FLAG_FORCE_TILE_MERGE if args.tile_merge else 0)
+    flags = (apd.FLAG_TIME_PHASES
+             | (apd.FLAG_FORCE_TILE_MERGE if args.tile_merge else 0)
+             | (apd.FLAG_PRUNE_TILES if args.prune else 0))
 
-    def step():
+    def step(fl):
         info = apd.dbscan_info()
         st = apd.dbscan_fit_device_ex(
             xt.data_ptr(), n, d, eps, min_pts, labels.data_ptr(),
-            counts.data_ptr(), ws.ptr, ws.nbytes, stream.cuda_stream, flags, info)
+            counts.data_ptr(), ws.ptr, ws.nbytes, stream.cuda_stream, fl, info)
         if st != 0:
             raise apd.DbscanError(st)
         return info
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    infos = []
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        infos.append(step())
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_region = start.elapsed_time(stop)
-    ms_per_step = ms_region / args.steps
+    def timed(fl, steps, warmup):
+        for _ in range(warmup):
+            step(fl)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        infos = []
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(steps):
+            infos.append(step(fl))
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return infos, start.elapsed_time(stop) / steps, wall
+
+    infos, ms_per_step, wall = timed(flags, args.steps, args.warmup)
 
     pairs = float(n) * float(n)
     value = pairs / (ms_per_step / 1e3)
@@ -166,6 +174,7 @@ def main():
     last = infos[-1]
 
     parity = "unchecked"
+    g = None
     if not args.no_parity:
         path = os.path.join(ROOT, "tests", "golden", "workloads.json")
         g = json.load(open(path)).get(str(args.workload)) if os.path.exists(path) else None
@@ -217,6 +226,29 @@ def main():
             "frac_distinct_pairs": achieved / 2 * (n - 1) / n / PEAK_FP32_TFLOPS,
         },
     }
+    out["config"]["tiles_kept"] = last.tiles_kept
+    out["config"]["tiles_total"] = last.tiles_total
+    if not args.prune and not args.no_pruned_line:
+        p_infos, p_ms, _ = timed(flags | apd.FLAG_PRUNE_TILES, args.steps, 1)
+        p_last = p_infos[-1]
+        p_parity = "unchecked"
+        if not args.no_parity and parity != "unchecked":
+            ok = (digest(labels.cpu().numpy()) == g["labels_sha256"]
+                  and digest(counts.cpu().numpy()) == g["counts_sha256"])
+            p_parity = "labels+counts bit-exact vs oracle" if ok else "MISMATCH vs oracle"
+        out["pruned_mode"] = {
+            "what": "same fit with exact tile pruning (DBSCAN_FLAG_PRUNE_TILES): "
+                    "block pairs whose fp32 box-gap bound exceeds eps^2 are "
+                    "skipped, every pair is still decided",
+            "value": pairs / (p_ms / 1e3),
+            "unit": "pair relations decided/s",
+            "ms_per_step": p_ms,
+            "ms_count": float(np.mean([i.ms_count for i in p_infos])),
+            "ms_layout_sort_boxes": float(np.mean([i.ms_layout for i in p_infos])),
+            "tiles_kept": p_last.tiles_kept,
+            "tiles_total": p_last.tiles_total,
+            "parity": p_parity,
+        }
     if args.host_entry:
         apd.fit_host(x, eps, min_pts)            # warm-up (allocations)
         t0 = time.perf_counter()

@@ -72,6 +72,16 @@ typedef enum dbscan_status {
                                          from HIP events on the stream */
 #define DBSCAN_FLAG_FORCE_TILE_MERGE 0x2u /* ignore the edge area and take the
                                              tile merge (for testing) */
+#define DBSCAN_FLAG_PRUNE_TILES 0x4u /* exact tile pruning: sort the points
+                                        along a space-filling curve, bound
+                                        each block of the count pass by its
+                                        box and skip block pairs whose fp32
+                                        box gap already exceeds eps^2 (a
+                                        lower bound of every distance
+                                        between them, in the same rounded
+                                        arithmetic); results are identical,
+                                        far fewer distances are evaluated
+                                        when d is small */
 
 /* What a fit did; filled by dbscan_fit_device_ex when info != NULL. */
 typedef struct dbscan_info {
@@ -83,6 +93,9 @@ typedef struct dbscan_info {
                             including padding: n_pad^2 */
   int64_t pass2_pairs;   /* distances evaluated by a tile merge (0 for the
                             edge merge) */
+  int64_t tiles_total;   /* block pairs (I <= J) of the count pass */
+  int64_t tiles_kept;    /* block pairs evaluated: all of them, or those
+                            left by DBSCAN_FLAG_PRUNE_TILES */
   int32_t merge_mode;    /* DBSCAN_MERGE_* */
   int32_t timed;         /* 1 if the ms_* fields below were measured */
   float ms_layout;       /* ingest, padding, non-finite check, init */

@@ -45,8 +45,8 @@ def test_abi_version_and_constants():
 
 
 def test_info_struct_matches_header_layout():
-    # 5 int64, 2 int32, 6 float, 2 int32
-    assert ctypes.sizeof(_capi.dbscan_info) == 5 * 8 + 2 * 4 + 6 * 4 + 2 * 4
+    # 7 int64, 2 int32, 6 float, 2 int32
+    assert ctypes.sizeof(_capi.dbscan_info) == 7 * 8 + 2 * 4 + 6 * 4 + 2 * 4
 
 
 def test_status_strings():

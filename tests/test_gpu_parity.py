@@ -51,7 +51,8 @@ def assert_same(got_l, got_c, want_l, want_c, what):
     assert bad_l.size == 0, f"{what}: {bad_l.size} labels differ, first {bad_l[:5]}"
 
 
-MODES = [(0, "edges"), (2, "tiles")]   # 2 = FLAG_FORCE_TILE_MERGE
+# 2 = FLAG_FORCE_TILE_MERGE, 4 = FLAG_PRUNE_TILES
+MODES = [(0, "edges"), (2, "tiles"), (4, "pruned"), (6, "pruned_tiles")]
 
 
 @pytest.mark.parametrize("flags,mode", MODES, ids=[m for _, m in MODES])
@@ -68,7 +69,7 @@ def test_small_random_vs_oracle(apd, orc, flags, mode):
         lab, cnt, info = gpu_fit(apd, x, eps, m, flags=flags)
         assert_same(lab, cnt, want_l, want_c, f"case {t} n={x.shape} eps={eps} m={m}")
         if x.shape[0] > 0 and info["n_core"] > 0:
-            want_mode = 2 if flags else 1
+            want_mode = 2 if flags & 2 else 1
             assert info["merge_mode"] == want_mode
 
 
@@ -96,6 +97,29 @@ def test_every_dimension(apd, orc):
         want_l, want_c, _ = orc.fit(x, eps, 5)
         lab, cnt, _ = gpu_fit(apd, x, eps, 5)
         assert_same(lab, cnt, want_l, want_c, f"d={d}")
+        lab, cnt, _ = gpu_fit(apd, x, eps, 5, flags=4)
+        assert_same(lab, cnt, want_l, want_c, f"d={d} pruned")
+
+
+def test_pruning_skips_tiles_exactly(apd, orc):
+    """Well separated blobs: most block pairs are pruned, results equal."""
+    for d, n in ((1, 60000), (2, 50000), (3, 40000), (8, 20000)):
+        x = datagen.gaussian_blobs(n, d, seed=500 + d, n_blobs=40, sigma=0.004,
+                                   noise_frac=0.05)
+        eps = 0.01
+        want_l, want_c, _ = orc.fit(x, eps, 6)
+        lab, cnt, info = gpu_fit(apd, x, eps, 6, flags=4)
+        assert_same(lab, cnt, want_l, want_c, f"d={d} n={n}")
+        assert info["tiles_kept"] < info["tiles_total"]
+        lab0, cnt0, info0 = gpu_fit(apd, x, eps, 6)
+        assert info0["tiles_kept"] == info0["tiles_total"]
+        assert info["n_edges"] == info0["n_edges"]
+    # ties at the radius between blocks: integer lattice, eps exactly 1
+    lat = datagen.integer_lattice(200, 2)
+    want_l, want_c, _ = orc.fit(lat, 1.0, 5)
+    lab, cnt, info = gpu_fit(apd, lat, 1.0, 5, flags=4)
+    assert_same(lab, cnt, want_l, want_c, "lattice pruned")
+    assert info["tiles_kept"] < info["tiles_total"]
 
 
 def test_boundary_ties(apd, orc):
@@ -219,11 +243,13 @@ def _digest(a):
     return hashlib.sha256(np.ascontiguousarray(a.astype("<i4")).tobytes()).hexdigest()
 
 
+@pytest.mark.parametrize("prune", [False, True], ids=["all_tiles", "pruned"])
 @pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
-def test_named_workload(apd, orc, key):
+def test_named_workload(apd, orc, key, prune):
     x, eps, m, w = datagen.make_workload(key)
-    print(f"workload {key} {w.name}", flush=True)
-    lab, cnt, info = gpu_fit(apd, x, eps, m, max_edges=1 << 30)
+    print(f"workload {key} {w.name} prune={prune}", flush=True)
+    lab, cnt, info = gpu_fit(apd, x, eps, m, max_edges=1 << 30,
+                             flags=4 if prune else 0)
     assert info["merge_mode"] == 1
     g = _golden().get(str(key))
     if g is not None and g["points_sha256"] == datagen.sha256_points(x):

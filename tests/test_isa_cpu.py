@@ -36,12 +36,13 @@ def asm(tmp_path_factory):
     return {
         "count": open(build.device_assembly(str(d / "c.s"), "k_count.hip")).read(),
         "merge": open(build.device_assembly(str(d / "m.s"), "k_merge.hip")).read(),
+        "prune": open(build.device_assembly(str(d / "p.s"), "k_prune.hip")).read(),
     }
 
 
 def test_count_kernels_have_no_fused_or_packed_fp32(asm):
     bodies = kernel_bodies(asm["count"], "k_count")
-    assert len(bodies) == 24          # 12 widths x (edges, no edges)
+    assert len(bodies) == 48   # 12 widths x (edges or not) x (pruned or not)
     for name, body in bodies.items():
         bad = FORBIDDEN.findall(body)
         assert not bad, (name, bad[:3])
@@ -56,8 +57,17 @@ def test_tile_merge_kernels_have_no_fused_or_packed_fp32(asm):
 
 
 def test_rows_are_scalar_loads(asm):
-    bodies = kernel_bodies(asm["count"], "k_countILi3ELb0")
+    bodies = kernel_bodies(asm["count"], "k_countILi3ELb0ELb0")
     (body,) = bodies.values()
     assert re.search(r"s_load_dword", body)
     # the distance takes its row operand straight from an SGPR
     assert re.search(r"v_sub_f32_e32 v\d+, s\d+, v\d+", body)
+
+
+def test_tile_bound_has_no_fused_fp32(asm):
+    """The box-gap bound must round like the distance: no FMA either."""
+    bodies = kernel_bodies(asm["prune"], "k_tile_list")
+    assert len(bodies) == 1
+    for name, body in bodies.items():
+        assert not FORBIDDEN.findall(body), name
+        assert "v_mul_f32" in body and "v_add_f32" in body
