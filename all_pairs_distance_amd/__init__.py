@@ -20,7 +20,8 @@ _C_NAMES = {
     "MERGE_NONE", "MERGE_TILES", "dbscan_abi_version", "dbscan_fit",
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_info",
     "dbscan_status_string", "dbscan_workspace_bytes",
-    "dbscan_workspace_bytes_with_edges",
+    "dbscan_workspace_bytes_with_edges", "dbscan_relabel_device",
+    "dbscan_relabel_workspace_bytes",
 }
 
 
@@ -38,7 +39,8 @@ __all__ = [
     "DbscanError", "Workspace", "fit", "fit_host", "dbscan_fit",
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_workspace_bytes",
     "dbscan_workspace_bytes_with_edges", "dbscan_status_string",
-    "dbscan_abi_version", "dbscan_info",
+    "dbscan_abi_version", "dbscan_info", "relabel",
+    "dbscan_relabel_device", "dbscan_relabel_workspace_bytes",
 ]
 
 
@@ -122,6 +124,33 @@ def fit(x, eps: float, min_pts: int, *, return_counts: bool = False,
     if return_info:
         out.append(info.as_dict())
     return out[0] if len(out) == 1 else tuple(out)
+
+
+def relabel(labels, return_sizes: bool = True, stream=None):
+    """Contiguous cluster ids 0..K-1 (ascending smallest member; noise -1)
+    for int32 device labels from ``fit``.  Returns ids, and the int32 sizes
+    of the K clusters if ``return_sizes``."""
+    import ctypes
+    import torch
+    c = _c()
+    if labels.dtype != torch.int32 or not labels.is_cuda:
+        raise TypeError("labels must be int32 on the GPU")
+    labels = labels.contiguous()
+    n = labels.numel()
+    ids = torch.empty_like(labels)
+    sizes = torch.empty(max(n, 1), dtype=torch.int32, device=labels.device)
+    ws = torch.empty(c.dbscan_relabel_workspace_bytes(n), dtype=torch.uint8,
+                     device=labels.device)
+    k = ctypes.c_int64(0)
+    if stream is None:
+        stream = torch.cuda.current_stream(labels.device)
+    st = c.dbscan_relabel_device(
+        labels.data_ptr() if n else None, n, ids.data_ptr() if n else None,
+        sizes.data_ptr() if return_sizes else None, k, ws.data_ptr(),
+        ws.numel(), stream.cuda_stream)
+    if st != 0:
+        raise DbscanError(st)
+    return (ids, sizes[:k.value]) if return_sizes else ids
 
 
 def fit_host(points, eps: float, min_pts: int, return_counts: bool = False):

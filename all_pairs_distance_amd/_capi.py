@@ -80,6 +80,12 @@ def _load() -> ctypes.CDLL:
     lib.dbscan_fit_device_ex.restype = ctypes.c_int
     lib.dbscan_fit.argtypes = [vp, i64, i32, f32, i32, vp, vp]
     lib.dbscan_fit.restype = ctypes.c_int
+    lib.dbscan_relabel_workspace_bytes.argtypes = [i64]
+    lib.dbscan_relabel_workspace_bytes.restype = ctypes.c_size_t
+    lib.dbscan_relabel_device.argtypes = [vp, i64, vp, vp,
+                                          ctypes.POINTER(ctypes.c_int64), vp,
+                                          ctypes.c_size_t, vp]
+    lib.dbscan_relabel_device.restype = ctypes.c_int
     lib.dbscan_status_string.argtypes = [ctypes.c_int]
     lib.dbscan_status_string.restype = ctypes.c_char_p
     lib.dbscan_abi_version.argtypes = []
@@ -121,6 +127,20 @@ def dbscan_fit(points: int, n: int, d: int, eps: float, min_pts: int,
                labels: int, counts: int | None) -> int:
     """Host-pointer entry: points/labels/counts are host addresses."""
     return int(lib.dbscan_fit(points, n, d, eps, min_pts, labels, counts))
+
+
+def dbscan_relabel_workspace_bytes(n: int) -> int:
+    return int(lib.dbscan_relabel_workspace_bytes(n))
+
+
+def dbscan_relabel_device(d_labels: int, n: int, d_ids: int,
+                          d_sizes: int | None, n_clusters, d_workspace: int,
+                          workspace_bytes: int, hip_stream: int | None) -> int:
+    """n_clusters: a ctypes.c_int64 (or None)."""
+    return int(lib.dbscan_relabel_device(
+        d_labels, n, d_ids, d_sizes,
+        ctypes.byref(n_clusters) if n_clusters is not None else None,
+        d_workspace, workspace_bytes, hip_stream))
 
 
 def dbscan_status_string(status: int) -> str:

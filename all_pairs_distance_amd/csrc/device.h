@@ -64,6 +64,26 @@ __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) 
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// Exclusive prefix sum over a 256-thread (4-wave) block; *total gets the
+// block's sum.  sh: 4 words of LDS.
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh,
+                                                    unsigned* total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  unsigned x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    unsigned y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  unsigned wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += sh[w];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return wbase + x - v;
+}
+
 // ---- union-find over point indices ---------------------------------------
 // parent[x] <= x always: a root is only ever hung under a smaller root (by a
 // device-scope CAS, which sees the current value), and path halving only

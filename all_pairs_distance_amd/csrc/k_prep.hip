@@ -96,25 +96,6 @@ hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
 // Blocks of 1024 points: per-block core totals, one exclusive scan over
 // the totals, then each block writes its cores in index order.
 
-__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh,
-                                                    unsigned* total) {
-  // 256 threads = 4 waves
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  unsigned x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    unsigned y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  unsigned wbase = 0;
-  for (int w = 0; w < wave; ++w) wbase += sh[w];
-  *total = sh[0] + sh[1] + sh[2] + sh[3];
-  __syncthreads();
-  return wbase + x - v;
-}
-
 __global__ __launch_bounds__(256) void k_core_block_totals(
     const unsigned char* __restrict__ core, int64_t n_pad,
     unsigned* __restrict__ sums) {

@@ -154,6 +154,26 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
 int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
                int32_t min_pts, int32_t* labels, int32_t* counts);
 
+/* Contiguous cluster ids from the labels of a fit: clusters are numbered
+ * 0..K-1 in ascending order of their label (their smallest member, so the
+ * numbering is as deterministic as the labels); noise stays -1.  A
+ * scan-based renumbering, as the Times-C summary (Sec. 3.1) computes class
+ * offsets.
+ *   d_labels  device, n int32 labels from dbscan_fit*; read only.
+ *   d_ids     device, n int32; written.
+ *   d_sizes   device, n int32 or NULL; sizes[k] = members of cluster k for
+ *             k < K (entries >= K untouched).
+ *   n_clusters host, K on return (may be NULL).
+ *   d_workspace at least dbscan_relabel_workspace_bytes(n), 256-aligned.
+ * Labels that are not smallest-member labels (l < -1, l >= n, or
+ * labels[l] != l) give DBSCAN_ERR_INVALID_ARG, detected on the device.
+ * Synchronises hip_stream before returning. */
+size_t dbscan_relabel_workspace_bytes(int64_t n);
+int dbscan_relabel_device(const int32_t* d_labels, int64_t n, int32_t* d_ids,
+                          int32_t* d_sizes, int64_t* n_clusters,
+                          void* d_workspace, size_t workspace_bytes,
+                          void* hip_stream);
+
 /* Static, never-NULL description of a status code. */
 const char* dbscan_status_string(int status);
 

@@ -74,6 +74,8 @@ class Oracle:
                                               ctypes.c_int64, i64p,
                                               ctypes.c_int64]
         lib.oracle_row_neighbours.restype = ctypes.c_int64
+        lib.oracle_relabel.argtypes = [i32p, ctypes.c_int64, i32p, i32p]
+        lib.oracle_relabel.restype = ctypes.c_int64
         lib.oracle_last_fit_seconds.argtypes = []
         lib.oracle_last_fit_seconds.restype = ctypes.c_double
         self.lib = lib
@@ -124,6 +126,20 @@ class Oracle:
                                    labels.ctypes.data_as(
                                        ctypes.POINTER(ctypes.c_int32)),
                                    None, 1)
+
+    def relabel(self, labels):
+        """Returns (contiguous ids int32[N], sizes int32[K], K)."""
+        lab = np.ascontiguousarray(labels, dtype=np.int32)
+        n = lab.size
+        out = np.empty(n, dtype=np.int32)
+        sizes = np.empty(max(n, 1), dtype=np.int32)
+        p = ctypes.POINTER(ctypes.c_int32)
+        k = self.lib.oracle_relabel(lab.ctypes.data_as(p), n,
+                                    out.ctypes.data_as(p),
+                                    sizes.ctypes.data_as(p))
+        if k < 0:
+            raise OracleError(int(k))
+        return out, sizes[:k].copy(), int(k)
 
     def row_counts(self, points, eps, rows, n_threads: int = 0) -> np.ndarray:
         x = self._pts(points)

@@ -264,3 +264,27 @@ int64_t oracle_row_neighbours(const float* p, int64_t n, int32_t d, float eps,
   }
   return c;
 }
+
+/* Number the clusters in ascending order of their label: a point whose
+ * label is its own index is the smallest member of its cluster; visiting
+ * points in ascending index meets those heads in ascending label order. */
+int64_t oracle_relabel(const int32_t* labels, int64_t n, int32_t* out,
+                       int32_t* sizes) {
+  if (n < 0 || (n > 0 && (labels == NULL || out == NULL))) return ORACLE_BAD_ARG;
+  int32_t* id = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+  if (!id) return ORACLE_NO_MEMORY;
+  int64_t k = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t l = labels[i];
+    if (l < -1 || l >= n || (l >= 0 && labels[l] != l)) { free(id); return ORACLE_BAD_ARG; }
+    if (l == i) id[i] = (int32_t)k++;
+  }
+  for (int64_t c = 0; sizes && c < k; ++c) sizes[c] = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t l = labels[i];
+    out[i] = l < 0 ? -1 : id[l];
+    if (l >= 0 && sizes) sizes[id[l]]++;
+  }
+  free(id);
+  return k;
+}

@@ -69,6 +69,13 @@ int oracle_row_counts(const float* points, int64_t n, int32_t d, float eps,
 int64_t oracle_row_neighbours(const float* points, int64_t n, int32_t d,
                               float eps, int64_t i, int64_t* out, int64_t cap);
 
+/* Contiguous cluster ids: clusters are numbered 0..K-1 in ascending order
+ * of their label (their smallest member); noise stays -1.  out: n int32.
+ * sizes: n int32 or NULL, sizes[k] = members of cluster k (entries >= K
+ * untouched).  Returns K, or a negative status. */
+int64_t oracle_relabel(const int32_t* labels, int64_t n, int32_t* out,
+                       int32_t* sizes);
+
 /* Wall time of the last oracle_fit on this thread, seconds (steady clock,
  * fit body only). */
 double oracle_last_fit_seconds(void);

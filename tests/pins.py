@@ -523,7 +523,28 @@ def check_argument_errors(o):
     assert o.fit_status(bad, 4, 2, 0.1, 1) == -2
 
 
+def check_relabel(o):
+    """Contiguous ids equal numpy.unique's inverse over the non-noise labels
+    (ascending label values), sizes its counts; on real oracle output and on
+    hand-made label vectors."""
+    cases = [np.array([-1, 1, 1, -1, 4, 1, 4, 7], np.int32),
+             np.array([], np.int32), np.array([-1, -1], np.int32),
+             np.array([0, 0, 0], np.int32)]
+    for x, eps, m in small_cases(seed=41, count=20):
+        cases.append(o.fit(x, eps, m)[0])
+    for lab in cases:
+        out, sizes, k = o.relabel(lab)
+        keep = lab >= 0
+        uniq, inv, cnt = np.unique(lab[keep], return_inverse=True,
+                                   return_counts=True)
+        want = np.full(lab.size, -1, np.int32)
+        want[keep] = inv
+        assert k == uniq.size
+        assert np.array_equal(out, want)
+        assert np.array_equal(sizes, cnt.astype(np.int32))
+
+
 ALL_CHECKS = [check_handworked, check_d2_exact, check_d2_order_and_rounding,
               check_eps2, check_bfs, check_invariants, check_sklearn,
               check_kdtree_counts, check_components, check_closed_forms,
-              check_argument_errors]
+              check_argument_errors, check_relabel]

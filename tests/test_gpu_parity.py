@@ -295,3 +295,24 @@ def test_named_workload_tile_merge(apd, key):
     b = gpu_fit(apd, x, eps, m, flags=2)
     assert b[2]["merge_mode"] == 2 and b[2]["pass2_pairs"] > 0
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_relabel_contiguous(apd, orc):
+    import torch
+    for t, (x, eps, m) in enumerate(pins.small_cases(seed=303, count=30)):
+        lab, _, _ = orc.fit(x, eps, m)
+        want_ids, want_sizes, k = orc.relabel(lab)
+        ids, sizes = apd.relabel(torch.from_numpy(lab).cuda())
+        assert np.array_equal(ids.cpu().numpy(), want_ids), t
+        assert np.array_equal(sizes.cpu().numpy(), want_sizes), t
+    for key in (2, 3):
+        x, eps, m, w = datagen.make_workload(key)
+        lab, _, _ = gpu_fit(apd, x, eps, m, max_edges=1 << 28)
+        want_ids, want_sizes, k = orc.relabel(lab)
+        ids, sizes = apd.relabel(torch.from_numpy(lab).cuda())
+        assert np.array_equal(ids.cpu().numpy(), want_ids), w.name
+        assert np.array_equal(sizes.cpu().numpy(), want_sizes), w.name
+    bad = torch.tensor([0, 0, 5, -1], dtype=torch.int32, device="cuda")
+    with pytest.raises(apd.DbscanError) as e:
+        apd.relabel(bad)
+    assert e.value.status == -1

@@ -50,6 +50,9 @@ MUTANTS = {
     # noise labelled 0 instead of -1
     "noise_zero": [("else { labels[i] = -1; continue; }",
                     "else { labels[i] = 0; continue; }")],
+    # relabelled noise becomes cluster 0
+    "relabel_noise_zero": [("out[i] = l < 0 ? -1 : id[l];",
+                            "out[i] = l < 0 ? 0 : id[l];")],
     # border points treated as noise
     "no_borders": [("else if (bmin[i] >= 0) r = uf_find(parent, bmin[i]);",
                     "else if (0) r = 0;")],
