@@ -34,7 +34,7 @@ static int64_t tile_capacity(int64_t n_pad, int D) {
   return all < kTileListCap ? all : kTileListCap;
 }
 
-constexpr int kRegions = 19;
+constexpr int kRegions = 21;
 
 // Region sizes in carve order; every region starts 256-byte aligned.
 static size_t regions(int64_t n_pad, int D, size_t* out) {
@@ -60,7 +60,9 @@ static size_t regions(int64_t n_pad, int D, size_t* out) {
       np * S * sizeof(float),        // sorted_pts
       nb * 2 * S * sizeof(float),    // boxes
       (size_t)tile_capacity(n_pad, D) * sizeof(uint2),  // tiles
-      sort_bytes(n_pad),             // radix sort scratch
+      np / 64 * 2 * S * sizeof(float),                   // boxes64
+      np / (64 * (size_t)lane_points(D)) * 2 * S * sizeof(float),  // boxes_w
+      sort_bytes(n_pad),             // radix sort scratch (last)
   };
   size_t total = 0;
   for (int r = 0; r < kRegions; ++r) {
@@ -100,8 +102,10 @@ bool carve(Layout& L, void* ws, size_t ws_bytes) {
   L.boxes = reinterpret_cast<float*>(b + off[16]);
   L.tiles = reinterpret_cast<uint2*>(b + off[17]);
   L.tile_cap = (unsigned long long)tile_capacity(L.n_pad, L.D);
-  L.sort_tmp = b + off[18];
-  L.sort_tmp_bytes = need - off[18];
+  L.boxes64 = reinterpret_cast<float*>(b + off[18]);
+  L.boxes_w = reinterpret_cast<float*>(b + off[19]);
+  L.sort_tmp = b + off[20];
+  L.sort_tmp_bytes = need - off[20];
   L.bytes_min = need;
   const size_t spare = ws_bytes - need;
   L.edges = reinterpret_cast<uint2*>(b + need);

@@ -64,6 +64,27 @@ __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) 
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// Lower bound of the fp32 distance between any point of box a and any point
+// of box b (each [lo[S], hi[S]]), in the distance's own rounded order: the
+// per-dimension gap is rounded like a difference, squared and summed in
+// ascending dimension.  Rounding is monotone, so every distance between
+// the two boxes is >= this bound.  True when the bound exceeds eps2.
+template <int S>
+__device__ __forceinline__ bool boxes_apart(const_float_ptr a, const_float_ptr b,
+                                            float eps2) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const float alo = a[k], ahi = a[S + k], blo = b[k], bhi = b[S + k];
+    float g = 0.f;
+    if (blo > ahi) g = blo - ahi;
+    else if (alo > bhi) g = alo - bhi;
+    const float q = g * g;
+    s = k == 0 ? q : s + q;
+  }
+  return s > eps2;
+}
+
 // Exclusive prefix sum over a 256-thread (4-wave) block; *total gets the
 // block's sum.  sh: 4 words of LDS.
 __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh,

@@ -72,6 +72,8 @@ struct Layout {
   int* perm;           // [n_pad] sorted position -> original index
   float* sorted_pts;   // [n_pad][stride] points in sorted order
   float* boxes;        // [nb][2][stride] block bounding boxes
+  float* boxes64;      // [n_pad/64][2][stride] boxes of 64-point row groups
+  float* boxes_w;      // [n_pad/(64P)][2][stride] boxes of a wave's columns
   uint2* tiles;        // kept block pairs
   unsigned long long tile_cap;
   void* sort_tmp;      // radix sort scratch

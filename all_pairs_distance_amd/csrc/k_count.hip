@@ -105,7 +105,9 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            unsigned* __restrict__ count,
                                            uint2* stage, unsigned& fill,
                                            const EdgeSink& sink,
-                                           const int* __restrict__ perm) {
+                                           const int* __restrict__ perm,
+                                           const float* __restrict__ boxes64,
+                                           const float* __restrict__ boxes_w) {
   constexpr int S = row_stride(D);
   const int lane = lane_id();
   float xc[P][D];
@@ -120,6 +122,15 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
   for (int p = 0; p < P; ++p) lc[p] = 0;
 
   for (int rb = 0; rb < rows; rb += 64) {
+    // pruned: skip 64 rows whose box is provably farther than eps from
+    // every column point of this wave (no neighbour among them); only for
+    // narrow points, where the test is a few scalar loads and the boxes
+    // are tight
+    if (PRUNED && D <= 16 &&
+        boxes_apart<S>((const_float_ptr)(boxes64 + ((row0 + rb) >> 6) * 2 * S),
+                       (const_float_ptr)(boxes_w + (colw / (64 * P)) * 2 * S),
+                       eps2))
+      continue;
     int rowv = 0;  // lane l: count of row rb+l over these columns
 #pragma unroll 1
     for (int l = 0; l < 64; ++l) {
@@ -192,7 +203,8 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES), 8))) void k_count(
     uint2* __restrict__ edges, unsigned long long cap,
     unsigned long long* __restrict__ counter,
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
-    unsigned long long tile_cap, const int* __restrict__ perm) {
+    unsigned long long tile_cap, const int* __restrict__ perm,
+    const float* __restrict__ boxes64, const float* __restrict__ boxes_w) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
@@ -225,10 +237,12 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES), 8))) void k_count(
     const int64_t colw = J * T + (int64_t)wave * 64 * P;
     if (I == J)
       count_item<D, P, true, EDGES, PRUNED>(pts, row0, rows, colw, eps2, count,
-                                            stage, fill, sink, perm);
+                                            stage, fill, sink, perm, boxes64,
+                                            boxes_w);
     else
       count_item<D, P, false, EDGES, PRUNED>(pts, row0, rows, colw, eps2,
-                                             count, stage, fill, sink, perm);
+                                             count, stage, fill, sink, perm,
+                                             boxes64, boxes_w);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
@@ -256,7 +270,8 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
 #define DBK_COUNT_ARGS                                                      \
   pts, nb, chunks_log2, rows, items, eps2, L.count,                         \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
-      &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm
+      &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
+      L.boxes_w
   if (edges && pruned)
     k_count<D, true, true><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
   else if (edges)

@@ -246,6 +246,12 @@ hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s) {
   const int64_t nb = L.n_pad / T;
   k_block_boxes<<<(unsigned)nb, 256, 0, s>>>(L.sorted_pts, L.perm, L.n, T,
                                              L.stride, L.boxes);
+  // finer boxes, tested inside the count pass: 64-point row groups and the
+  // 64*P columns one wave holds
+  k_block_boxes<<<(unsigned)(L.n_pad / 64), 256, 0, s>>>(
+      L.sorted_pts, L.perm, L.n, 64, L.stride, L.boxes64);
+  k_block_boxes<<<(unsigned)(L.n_pad / (T / 4)), 256, 0, s>>>(
+      L.sorted_pts, L.perm, L.n, T / 4, L.stride, L.boxes_w);
   const int64_t tiles = nb * (nb + 1) / 2;
   k_tile_list<<<grid_for_p(tiles, 256), 256, 0, s>>>(
       L.boxes, nb, L.stride, eps2, L.tiles, L.tile_cap, L.status);
