@@ -76,6 +76,12 @@ class Oracle:
         lib.oracle_row_neighbours.restype = ctypes.c_int64
         lib.oracle_relabel.argtypes = [i32p, ctypes.c_int64, i32p, i32p]
         lib.oracle_relabel.restype = ctypes.c_int64
+        lib.oracle_graph.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.c_float, i64p,
+                                     ctypes.POINTER(i32p), ctypes.c_int32]
+        lib.oracle_graph.restype = ctypes.c_int64
+        lib.oracle_free.argtypes = [ctypes.c_void_p]
+        lib.oracle_free.restype = None
         lib.oracle_last_fit_seconds.argtypes = []
         lib.oracle_last_fit_seconds.restype = ctypes.c_double
         self.lib = lib
@@ -140,6 +146,27 @@ class Oracle:
         if k < 0:
             raise OracleError(int(k))
         return out, sizes[:k].copy(), int(k)
+
+    def graph(self, points, eps, n_threads: int = 0):
+        """Sparse eps-graph: (row_ptr int64[n+1], col_idx int32[nnz])."""
+        x = self._pts(points)
+        n, d = x.shape
+        row_ptr = np.zeros(n + 1, dtype=np.int64)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        col = i32p()
+        nnz = self.lib.oracle_graph(
+            x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n, d,
+            float(np.float32(eps)),
+            row_ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            ctypes.byref(col), int(n_threads))
+        if nnz < 0:
+            raise OracleError(int(nnz))
+        try:
+            col_idx = (np.ctypeslib.as_array(col, shape=(nnz,)).copy()
+                       if nnz > 0 else np.zeros(0, dtype=np.int32))
+        finally:
+            self.lib.oracle_free(col)
+        return row_ptr, col_idx
 
     def row_counts(self, points, eps, rows, n_threads: int = 0) -> np.ndarray:
         x = self._pts(points)

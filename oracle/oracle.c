@@ -288,3 +288,75 @@ int64_t oracle_relabel(const int32_t* labels, int64_t n, int32_t* out,
   free(id);
   return k;
 }
+
+/* Sparse epsilon-graph.  Row i lists every j with d2(i, j) <= eps2,
+ * itself included, in ascending j: the per-point neighbourhoods that Wang
+ * et al. Sec. IV-B keep as rows of their N x N cluster matrix, stored
+ * without the zeros.  Each row is found by a plain scan over all points,
+ * rows in parallel, each into its own list; the lists are then laid out
+ * one after another. */
+int64_t oracle_graph(const float* p, int64_t n, int32_t d, float eps,
+                     int64_t* row_ptr, int32_t** col_idx_out,
+                     int32_t n_threads) {
+  int st = check_args(p, n, d, eps, 1);
+  if (st != ORACLE_OK) return st;
+  if (row_ptr == NULL || col_idx_out == NULL) return ORACLE_BAD_ARG;
+  *col_idx_out = NULL;
+  if (host_flushes_denormals()) return ORACLE_FTZ_SET;
+  st = check_finite(p, n, d);
+  if (st != ORACLE_OK) return st;
+  row_ptr[0] = 0;
+  if (n == 0) return 0;
+  const float eps2 = oracle_eps2(eps);
+  const int nt = thread_count(n_threads);
+  int32_t** rows = (int32_t**)calloc((size_t)n, sizeof(int32_t*));
+  int64_t* len = (int64_t*)calloc((size_t)n, sizeof(int64_t));
+  int oom = (rows == NULL || len == NULL);
+  if (!oom) {
+#pragma omp parallel num_threads(nt)
+    {
+      int32_t* tmp = (int32_t*)malloc((size_t)n * sizeof(int32_t));
+      if (tmp == NULL) {
+#pragma omp atomic write
+        oom = 1;
+      }
+#pragma omp for schedule(dynamic, 64)
+      for (int64_t i = 0; i < n; ++i) {
+        if (tmp == NULL) continue;
+        const float* pi = p + i * (int64_t)d;
+        int64_t c = 0;
+        for (int64_t j = 0; j < n; ++j)
+          if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++] = (int32_t)j;
+        rows[i] = (int32_t*)malloc((size_t)c * sizeof(int32_t));
+        if (rows[i] == NULL) {
+#pragma omp atomic write
+          oom = 1;
+          continue;
+        }
+        memcpy(rows[i], tmp, (size_t)c * sizeof(int32_t));
+        len[i] = c;
+      }
+      free(tmp);
+    }
+  }
+  int32_t* col = NULL;
+  if (!oom) {
+    for (int64_t i = 0; i < n; ++i) row_ptr[i + 1] = row_ptr[i] + len[i];
+    col = (int32_t*)malloc((size_t)row_ptr[n] * sizeof(int32_t));
+    if (col == NULL) oom = 1;
+  }
+  if (!oom)
+    for (int64_t i = 0; i < n; ++i)
+      memcpy(col + row_ptr[i], rows[i], (size_t)len[i] * sizeof(int32_t));
+  for (int64_t i = 0; rows && i < n; ++i) free(rows[i]);
+  free(rows);
+  free(len);
+  if (oom) {
+    free(col);
+    return ORACLE_NO_MEMORY;
+  }
+  *col_idx_out = col;
+  return row_ptr[n];
+}
+
+void oracle_free(void* ptr) { free(ptr); }

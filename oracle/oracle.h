@@ -76,6 +76,16 @@ int64_t oracle_row_neighbours(const float* points, int64_t n, int32_t d,
 int64_t oracle_relabel(const int32_t* labels, int64_t n, int32_t* out,
                        int32_t* sizes);
 
+/* Sparse epsilon-graph in CSR form: row i holds every j with
+ * d2(i, j) <= eps2, itself included, in ascending j.  row_ptr: n+1 int64
+ * (written).  *col_idx_out receives a malloc'd int32 array of row_ptr[n]
+ * entries (release it with oracle_free); NULL on error.  Returns the
+ * number of entries, or a negative status. */
+int64_t oracle_graph(const float* points, int64_t n, int32_t d, float eps,
+                     int64_t* row_ptr, int32_t** col_idx_out,
+                     int32_t n_threads);
+void oracle_free(void* ptr);
+
 /* Wall time of the last oracle_fit on this thread, seconds (steady clock,
  * fit body only). */
 double oracle_last_fit_seconds(void);

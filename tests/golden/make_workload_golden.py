@@ -2,7 +2,9 @@
 synthetic workloads, as SHA-256 digests and summary counts.
 
 Only the oracle is called (never the GPU library).  Run from the repository
-root:  python tests/golden/make_workload_golden.py [--threads T] [keys...]
+root:  python tests/golden/make_workload_golden.py [--threads T] [--graph]
+[keys...]   (--graph adds the digest of the sparse eps-graph to existing
+entries, leaving the fit's fields as they are)
 Each workload is written as soon as it finishes, so a partial run keeps its
 finished entries.  The GPU parity tests compare the library's labels and
 neighbour counts with these digests bit for bit, after checking that the
@@ -34,6 +36,15 @@ def digest(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
 
 
+def graph_digest(row_ptr: np.ndarray, col_idx: np.ndarray) -> str:
+    """SHA-256 over row_ptr (little-endian int64) followed by col_idx
+    (little-endian int32)."""
+    h = hashlib.sha256()
+    h.update(np.ascontiguousarray(row_ptr.astype("<i8")).tobytes())
+    h.update(np.ascontiguousarray(col_idx.astype("<i4")).tobytes())
+    return h.hexdigest()
+
+
 def summary(labels: np.ndarray, counts: np.ndarray, min_pts: int) -> dict:
     core = counts >= min_pts
     noise = labels == -1
@@ -50,6 +61,7 @@ def summary(labels: np.ndarray, counts: np.ndarray, min_pts: int) -> dict:
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--graph", action="store_true")
     ap.add_argument("keys", nargs="*", type=int, default=[1, 2, 3, 4, 5])
     args = ap.parse_args()
     table = {}
@@ -61,6 +73,19 @@ def main() -> None:
         x, eps, min_pts, w = datagen.make_workload(k)
         print(f"workload {k} {w.name}: n={w.n} d={w.d}", flush=True)
         t0 = time.time()
+        if args.graph:
+            entry = table[str(k)]
+            assert entry["points_sha256"] == datagen.sha256_points(x)
+            row_ptr, col_idx = o.graph(x, eps, n_threads=args.threads)
+            entry["graph_sha256"] = graph_digest(row_ptr, col_idx)
+            entry["graph_nnz"] = int(row_ptr[-1])
+            del row_ptr, col_idx
+            with open(OUT, "w") as f:
+                json.dump(table, f, indent=1, sort_keys=True)
+                f.write("\n")
+            print(k, entry["graph_nnz"], f"wall {time.time() - t0:.1f}s",
+                  flush=True)
+            continue
         labels, counts, fit_s = o.fit(x, eps, min_pts, n_threads=args.threads)
         entry = {
             "name": w.name, "n": w.n, "d": w.d, "eps": w.eps,

@@ -544,7 +544,60 @@ def check_relabel(o):
         assert np.array_equal(sizes, cnt.astype(np.int32))
 
 
+def load_graph_cases():
+    with open(os.path.join(GOLDEN, "handworked.json")) as f:
+        cases = json.load(f)["graph_cases"]
+    return [(c["id"], np.array(c["points"], dtype=np.float32), c["eps"],
+             np.array(c["row_ptr"], np.int64), np.array(c["col_idx"], np.int32))
+            for c in cases]
+
+
+def check_graph_structure(x, eps, row_ptr, col_idx):
+    """CSR well-formed: monotone offsets, rows sorted ascending and free of
+    repeats, every point in its own row, and the relation symmetric."""
+    n = x.shape[0]
+    assert row_ptr.shape == (n + 1,) and row_ptr[0] == 0
+    assert col_idx.shape == (int(row_ptr[-1]),)
+    assert np.all(np.diff(row_ptr) >= 1)
+    pairs = set()
+    for i in range(n):
+        r = col_idx[row_ptr[i]:row_ptr[i + 1]]
+        assert np.all(np.diff(r) > 0), i
+        assert i in set(r.tolist()), i
+        pairs.update((i, int(j)) for j in r)
+    assert all((j, i) in pairs for i, j in pairs)
+
+
+def check_graph(o):
+    """The eps-graph equals, row by row, the neighbour lists found by the
+    float32 step emulation (hand-worked cases, random small sets with ties
+    and duplicates), and scipy's k-d tree ball lists on inputs with no pair
+    near the radius; every result is a well-formed symmetric CSR."""
+    for cid, x, eps, rp, ci in load_graph_cases():
+        row_ptr, col_idx = o.graph(x, eps)
+        assert np.array_equal(row_ptr, rp), (cid, row_ptr)
+        assert np.array_equal(col_idx, ci), (cid, col_idx)
+    for x, eps, _ in small_cases(seed=43, count=30):
+        row_ptr, col_idx = o.graph(x, eps)
+        check_graph_structure(x, eps, row_ptr, col_idx)
+        lists = neighbour_lists(x, eps)
+        want_ptr = np.concatenate([[0], np.cumsum([len(v) for v in lists])])
+        assert np.array_equal(row_ptr, want_ptr), (x.shape, eps)
+        assert np.array_equal(col_idx, np.concatenate(lists).astype(np.int32))
+    from scipy.spatial import cKDTree
+    for x, eps, _ in clean_blob_cases(seed=47, count=6):
+        row_ptr, col_idx = o.graph(x, eps)
+        tree = cKDTree(x.astype(np.float64))
+        balls = tree.query_ball_point(x.astype(np.float64),
+                                      r=float(np.float32(eps)))
+        for i, b in enumerate(balls):
+            assert np.array_equal(col_idx[row_ptr[i]:row_ptr[i + 1]],
+                                  np.array(sorted(b), np.int32)), i
+    row_ptr, col_idx = o.graph(np.zeros((0, 3), np.float32), 0.1)
+    assert row_ptr.tolist() == [0] and col_idx.size == 0
+
+
 ALL_CHECKS = [check_handworked, check_d2_exact, check_d2_order_and_rounding,
               check_eps2, check_bfs, check_invariants, check_sklearn,
               check_kdtree_counts, check_components, check_closed_forms,
-              check_argument_errors, check_relabel]
+              check_argument_errors, check_relabel, check_graph]

@@ -53,6 +53,17 @@ MUTANTS = {
     # relabelled noise becomes cluster 0
     "relabel_noise_zero": [("out[i] = l < 0 ? -1 : id[l];",
                             "out[i] = l < 0 ? 0 : id[l];")],
+    # graph rows leave out the point itself
+    "graph_no_self": [("if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++] = (int32_t)j;",
+                       "if (j != i && oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++] = (int32_t)j;")],
+    # graph rows scanned in descending order
+    "graph_descending": [("        for (int64_t j = 0; j < n; ++j)\n          if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++]",
+                          "        for (int64_t j = n - 1; j >= 0; --j)\n          if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++]")],
+    # graph radius made strict (only in the graph)
+    "graph_strict": [("<= eps2) tmp[c++]", "< eps2) tmp[c++]")],
+    # graph offsets shifted by one row
+    "graph_offsets": [("row_ptr[i + 1] = row_ptr[i] + len[i];",
+                       "row_ptr[i + 1] = row_ptr[i] + (i + 1 < n ? len[i + 1] : len[0]);")],
     # border points treated as noise
     "no_borders": [("else if (bmin[i] >= 0) r = uf_find(parent, bmin[i]);",
                     "else if (0) r = 0;")],
