@@ -21,7 +21,8 @@ _C_NAMES = {
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_info",
     "dbscan_status_string", "dbscan_workspace_bytes",
     "dbscan_workspace_bytes_with_edges", "dbscan_relabel_device",
-    "dbscan_relabel_workspace_bytes",
+    "dbscan_relabel_workspace_bytes", "dbscan_graph_device",
+    "dbscan_graph_workspace_bytes", "ERR_CAPACITY", "ERR_WORKSPACE",
 }
 
 
@@ -40,7 +41,8 @@ __all__ = [
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_workspace_bytes",
     "dbscan_workspace_bytes_with_edges", "dbscan_status_string",
     "dbscan_abi_version", "dbscan_info", "relabel",
-    "dbscan_relabel_device", "dbscan_relabel_workspace_bytes",
+    "dbscan_relabel_device", "dbscan_relabel_workspace_bytes", "graph",
+    "dbscan_graph_device", "dbscan_graph_workspace_bytes",
 ]
 
 
@@ -124,6 +126,53 @@ def fit(x, eps: float, min_pts: int, *, return_counts: bool = False,
     if return_info:
         out.append(info.as_dict())
     return out[0] if len(out) == 1 else tuple(out)
+
+
+def graph(x, eps: float, *, max_pairs: int | None = None, flags: int = 0,
+          return_info: bool = False, stream=None):
+    """Sparse eps-graph of the rows of ``x`` (torch float32 [N, d] on the
+    GPU) in CSR form: returns int64 ``row_ptr`` [N+1] and int32 ``col_idx``
+    [nnz] on the device; row i lists every j with d2(i, j) <= eps^2, i
+    itself included, in ascending j.  ``max_pairs`` sizes the first attempt
+    (neighbour pairs i<j); when the graph is larger the call is repeated
+    once with the sizes the library reported."""
+    import ctypes
+    import torch
+    c = _c()
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32:
+        raise TypeError("x must be a torch.float32 tensor")
+    if x.dim() == 1:
+        x = x.reshape(-1, 1)
+    if x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [N, d] tensor on the GPU")
+    n, d = x.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    if max_pairs is None:
+        max_pairs = min(64 * n, default_edge_capacity(x.device))
+    row_ptr = torch.empty(n + 1, dtype=torch.int64, device=x.device)
+    for attempt in range(2):
+        nbytes = c.dbscan_graph_workspace_bytes(n, d, max_pairs)
+        if nbytes == 0:
+            raise DbscanError(c.ERR_INVALID_ARG)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+        col = torch.empty(max(n + 2 * max_pairs, 1), dtype=torch.int32,
+                          device=x.device)
+        nnz = ctypes.c_int64(0)
+        info = c.dbscan_info()
+        st = c.dbscan_graph_device(
+            x.data_ptr() if n else None, n, d, float(eps), row_ptr.data_ptr(),
+            col.data_ptr(), col.numel(), nnz, ws.data_ptr(), ws.numel(),
+            stream.cuda_stream, int(flags), info)
+        if attempt == 0 and st in (c.ERR_CAPACITY, c.ERR_WORKSPACE):
+            max_pairs = int(info.n_edges)
+            del ws, col
+            continue
+        break
+    if st != 0:
+        raise DbscanError(st, info.hip_error)
+    out = (row_ptr, col[:nnz.value])
+    return out + (info.as_dict(),) if return_info else out
 
 
 def relabel(labels, return_sizes: bool = True, stream=None):

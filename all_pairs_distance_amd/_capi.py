@@ -19,6 +19,7 @@ ERR_NO_DEVICE = -3
 ERR_OOM = -4
 ERR_WORKSPACE = -5
 ERR_HIP = -6
+ERR_CAPACITY = -7
 
 MERGE_NONE, MERGE_EDGES, MERGE_TILES = 0, 1, 2
 FLAG_TIME_PHASES = 0x1
@@ -86,6 +87,13 @@ def _load() -> ctypes.CDLL:
                                           ctypes.POINTER(ctypes.c_int64), vp,
                                           ctypes.c_size_t, vp]
     lib.dbscan_relabel_device.restype = ctypes.c_int
+    lib.dbscan_graph_workspace_bytes.argtypes = [i64, i32, i64]
+    lib.dbscan_graph_workspace_bytes.restype = ctypes.c_size_t
+    lib.dbscan_graph_device.argtypes = [vp, i64, i32, f32, vp, vp, i64,
+                                        ctypes.POINTER(ctypes.c_int64), vp,
+                                        ctypes.c_size_t, vp, ctypes.c_uint32,
+                                        ctypes.POINTER(dbscan_info)]
+    lib.dbscan_graph_device.restype = ctypes.c_int
     lib.dbscan_status_string.argtypes = [ctypes.c_int]
     lib.dbscan_status_string.restype = ctypes.c_char_p
     lib.dbscan_abi_version.argtypes = []
@@ -141,6 +149,23 @@ def dbscan_relabel_device(d_labels: int, n: int, d_ids: int,
         d_labels, n, d_ids, d_sizes,
         ctypes.byref(n_clusters) if n_clusters is not None else None,
         d_workspace, workspace_bytes, hip_stream))
+
+
+def dbscan_graph_workspace_bytes(n: int, d: int, max_pairs: int) -> int:
+    return int(lib.dbscan_graph_workspace_bytes(n, d, max_pairs))
+
+
+def dbscan_graph_device(d_points: int, n: int, d: int, eps: float,
+                        d_row_ptr: int, d_col_idx: int | None,
+                        col_capacity: int, nnz_out, d_workspace: int,
+                        workspace_bytes: int, hip_stream: int | None,
+                        flags: int = 0, info: dbscan_info | None = None) -> int:
+    """nnz_out: a ctypes.c_int64 (or None)."""
+    return int(lib.dbscan_graph_device(
+        d_points, n, d, eps, d_row_ptr, d_col_idx, col_capacity,
+        ctypes.byref(nnz_out) if nnz_out is not None else None,
+        d_workspace, workspace_bytes, hip_stream, flags,
+        ctypes.byref(info) if info is not None else None))
 
 
 def dbscan_status_string(status: int) -> str:

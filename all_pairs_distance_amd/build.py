@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libdbscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "k_count.hip", "k_prep.hip", "k_merge.hip",
-           "k_prune.hip", "k_relabel.hip"]
+           "k_prune.hip", "k_relabel.hip", "k_graph.hip"]
 HEADERS = ["internal.h", "device.h"]
 ARCH = "gfx950"
 FLAGS = [

@@ -185,6 +185,44 @@ struct PhaseTimer {
     }                                     \
   } while (0)
 
+// Graph export: after the fit's regions come the row cursors, the
+// row-offset scan totals and the segmented-sort scratch; the rest of the
+// workspace holds the captured pairs and, once they are scattered, serves
+// as the sort's second buffer (4 bytes per graph entry: 4n + 8 per pair).
+size_t graph_sort_reserve(int64_t n_pad) {
+  size_t b = graph_sort_bytes(n_pad);
+  // the size query needs a device; without one, a generous estimate
+  if (b == 0) b = (size_t)n_pad * 16 + ((size_t)1 << 20);
+  return b;
+}
+
+size_t graph_fixed_bytes(int64_t n_pad) {
+  return align_up((size_t)n_pad * sizeof(unsigned), 256) +
+         align_up(((size_t)n_pad / 1024 + 2) * sizeof(unsigned long long), 256) +
+         align_up(graph_sort_reserve(n_pad), 256);
+}
+
+bool carve_graph(Layout& L, GraphLayout& G, void* ws, size_t ws_bytes) {
+  if (!carve(L, ws, ws_bytes)) return false;
+  const size_t spare = ws_bytes - L.bytes_min;
+  const size_t fixed = graph_fixed_bytes(L.n_pad);
+  const size_t alt_min = (size_t)L.n_pad * sizeof(int);
+  if (spare < fixed + alt_min) return false;
+  char* b = static_cast<char*>(ws) + L.bytes_min;
+  G.cursor = reinterpret_cast<unsigned*>(b);
+  b += align_up((size_t)L.n_pad * sizeof(unsigned), 256);
+  G.row_sums = reinterpret_cast<unsigned long long*>(b);
+  b += align_up(((size_t)L.n_pad / 1024 + 2) * sizeof(unsigned long long), 256);
+  G.sort_tmp = b;
+  G.sort_bytes = graph_sort_reserve(L.n_pad);
+  b += align_up(G.sort_bytes, 256);
+  const size_t rest = spare - fixed;
+  G.alt = b;
+  L.edges = reinterpret_cast<uint2*>(b);
+  L.edge_cap = (rest - alt_min) / sizeof(uint2);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,6 +250,7 @@ const char* dbscan_status_string(int status) {
     case DBSCAN_ERR_OOM: return "device memory allocation failed";
     case DBSCAN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case DBSCAN_ERR_HIP: return "HIP runtime error";
+    case DBSCAN_ERR_CAPACITY: return "output buffer too small (size reported)";
     default: return "unknown status";
   }
 }
@@ -381,6 +420,121 @@ int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
   if (d_pts) (void)hipFree(d_pts);
   (void)hipStreamDestroy(stream);
   return rc;
+}
+
+size_t dbscan_graph_workspace_bytes(int64_t n, int32_t d, int64_t max_pairs) {
+  const size_t base = dbscan_workspace_bytes(n, d);
+  if (base == 0 || max_pairs < 0) return 0;
+  const int64_t n_pad = pad_points(n < 1 ? 1 : n);
+  return base + graph_fixed_bytes(n_pad) +
+         align_up((size_t)n_pad * sizeof(int) + (size_t)max_pairs * sizeof(uint2),
+                  256);
+}
+
+int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
+                        int64_t* d_row_ptr, int32_t* d_col_idx,
+                        int64_t col_capacity, int64_t* nnz_out,
+                        void* d_workspace, size_t workspace_bytes,
+                        void* hip_stream, uint32_t flags, dbscan_info* info) {
+  if (info) std::memset(info, 0, sizeof(*info));
+  int st = check_args(n, d, eps, 1);
+  if (st != DBSCAN_OK) return st;
+  if (flags & ~(DBSCAN_FLAG_TIME_PHASES | DBSCAN_FLAG_PRUNE_TILES))
+    return DBSCAN_ERR_INVALID_ARG;
+  if (d_row_ptr == nullptr || col_capacity < 0 ||
+      (col_capacity > 0 && d_col_idx == nullptr) ||
+      (n > 0 && d_points == nullptr))
+    return DBSCAN_ERR_INVALID_ARG;
+  st = have_device();
+  if (st != DBSCAN_OK) return st;
+  (void)hipGetLastError();
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (n == 0) {
+    const int64_t zero = 0;
+    DB_TRY(hipMemcpyAsync(d_row_ptr, &zero, sizeof(zero),
+                          hipMemcpyHostToDevice, stream));
+    DB_TRY(hipStreamSynchronize(stream));
+    if (nnz_out) *nnz_out = 0;
+    return DBSCAN_OK;
+  }
+
+  Layout L{};
+  GraphLayout G{};
+  L.n = n;
+  L.d = d;
+  L.D = pick_dim(d);
+  L.stride = row_stride(L.D);
+  L.n_pad = pad_points(n);
+  if (!carve_graph(L, G, d_workspace, workspace_bytes))
+    return DBSCAN_ERR_WORKSPACE;
+  const size_t sort_need = graph_sort_bytes(n);
+  if (sort_need > G.sort_bytes) return DBSCAN_ERR_HIP;
+
+  volatile float eps_v = eps;
+  const float eps2 = eps_v * eps_v;
+  const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
+  const unsigned long long col_cap = (unsigned long long)col_capacity;
+  PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
+  int64_t pass1 = 0;
+
+  tm.mark(0);
+  DB_TRY(launch_prepare(L, d_points, stream));
+  if (prune) DB_TRY(launch_prune(L, block_points(L.D), eps2, stream));
+  tm.mark(1);
+  DB_TRY(launch_count(L, eps2, true, prune, stream, &pass1));
+  tm.mark(2);
+  DB_TRY(launch_row_offsets(L, G, d_row_ptr, d_col_idx, col_cap, stream));
+  Status host_st;
+  int64_t nnz = 0;
+  DB_TRY(hipMemcpyAsync(&host_st, L.status, sizeof(Status),
+                        hipMemcpyDeviceToHost, stream));
+  DB_TRY(hipMemcpyAsync(&nnz, d_row_ptr + n, sizeof(nnz),
+                        hipMemcpyDeviceToHost, stream));
+  DB_TRY(hipStreamSynchronize(stream));
+  if (host_st.nonfinite) return DBSCAN_ERR_NONFINITE;
+  const unsigned long long n_pairs = host_st.n_edges;
+  if (nnz_out) *nnz_out = nnz;
+  if (info) {
+    info->n_edges = (int64_t)n_pairs;
+    info->edge_capacity = (int64_t)L.edge_cap;
+    const int64_t nb = L.n_pad / block_points(L.D);
+    info->tiles_total = nb * (nb + 1) / 2;
+    info->tiles_kept = prune && host_st.n_tiles <= L.tile_cap
+                           ? (int64_t)host_st.n_tiles
+                           : info->tiles_total;
+    info->pass1_pairs = pass1;
+    info->merge_mode = DBSCAN_MERGE_EDGES;
+  }
+  // every row holds its point and one entry per pair it belongs to
+  if ((unsigned long long)nnz != (unsigned long long)n + 2ull * n_pairs)
+    return DBSCAN_ERR_HIP;
+  if (nnz >= ((int64_t)1 << 32) || (unsigned long long)nnz > col_cap)
+    return DBSCAN_ERR_CAPACITY;
+  if (n_pairs > L.edge_cap) return DBSCAN_ERR_WORKSPACE;
+
+  tm.mark(3);
+  DB_TRY(launch_graph_scatter(L, G, n_pairs, d_row_ptr, d_col_idx, stream));
+  tm.mark(4);
+  bool in_alt = false;
+  DB_TRY(launch_graph_sort(L, G, d_row_ptr, d_col_idx, nnz, &in_alt, stream));
+  if (in_alt)
+    DB_TRY(hipMemcpyAsync(d_col_idx, G.alt, (size_t)nnz * sizeof(int32_t),
+                          hipMemcpyDeviceToDevice, stream));
+  tm.mark(5);
+  DB_TRY(hipMemcpyAsync(&host_st, L.status, sizeof(Status),
+                        hipMemcpyDeviceToHost, stream));
+  DB_TRY(hipStreamSynchronize(stream));
+  if (host_st.graph_bad) return DBSCAN_ERR_HIP;
+  if (info && tm.on) {
+    info->timed = 1;
+    info->ms_layout = tm.ms(0, 1);
+    info->ms_count = tm.ms(1, 2);
+    info->ms_core = tm.ms(2, 3);
+    info->ms_merge = tm.ms(3, 4);
+    info->ms_label = tm.ms(4, 5);
+    info->ms_total = tm.ms(0, 5);
+  }
+  return DBSCAN_OK;
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ struct Status {
   unsigned int n_core;             // number of core points
   unsigned long long n_edges;      // edge slots reserved by the count pass
   unsigned int n_core_list;        // entries written by the core compaction
-  unsigned int pad0;
+  unsigned int graph_bad;           // a graph slot fell outside its row
   unsigned long long n_tiles;      // block pairs kept by the tile pruning
   unsigned int pad[8];
 };
@@ -83,6 +83,15 @@ struct Layout {
   size_t bytes_min;    // minimum workspace
 };
 
+// Extra regions of a graph export, carved after the fit's layout.
+struct GraphLayout {
+  unsigned* cursor;              // [n] next free slot of each row
+  unsigned long long* row_sums;  // [n / 1024 + 1] row-offset scan
+  void* sort_tmp;                // segmented sort scratch
+  size_t sort_bytes;
+  void* alt;                     // second sort buffer (overlays the pairs)
+};
+
 size_t layout_min_bytes(int64_t n, int d);
 bool carve(Layout& L, void* ws, size_t ws_bytes);
 
@@ -100,5 +109,16 @@ hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
 hipError_t launch_merge_tiles(const Layout& L, float eps2, int64_t n_core,
                               hipStream_t s, int64_t* pairs);
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);
+size_t graph_sort_bytes(int64_t n);
+hipError_t launch_row_offsets(const Layout& L, const GraphLayout& G,
+                              int64_t* row_ptr, int* col_idx,
+                              unsigned long long col_cap, hipStream_t s);
+hipError_t launch_graph_scatter(const Layout& L, const GraphLayout& G,
+                                unsigned long long n_pairs,
+                                const int64_t* row_ptr, int* col_idx,
+                                hipStream_t s);
+hipError_t launch_graph_sort(const Layout& L, const GraphLayout& G,
+                             const int64_t* row_ptr, int* col_idx, int64_t nnz,
+                             bool* in_alt, hipStream_t s);
 
 }  // namespace dbk

@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--prune", action="store_true",
                     help="time the exact tile-pruned fit as the main line")
+    ap.add_argument("--no-graph-line", action="store_true",
+                    help="skip the sparse eps-graph export leg")
     ap.add_argument("--no-pruned-line", action="store_true",
                     help="skip the extra pruned_mode measurement")
     ap.add_argument("--host-entry", action="store_true",
@@ -106,6 +108,72 @@ def cpu_baseline(x, eps, min_pts, target_s):
             "cores": threads, "kind": "oracle",
             "sample": f"full oracle fit of the first {m} points of the "
                       f"workload ({t:.1f} s)"}
+
+
+def graph_leg(apd, torch, xt, n, d, eps, stream, steps, g, no_parity):
+    """Time the sparse eps-graph export (pruned count pass, then row
+    offsets, pair scatter and row sort) with buffers of the exact size,
+    learnt from one sizing call."""
+    import ctypes
+    c = apd._c()
+    flags = apd.FLAG_PRUNE_TILES | apd.FLAG_TIME_PHASES
+    row_ptr = torch.empty(n + 1, dtype=torch.int64, device=xt.device)
+
+    def call(ws, col, cap):
+        nnz = ctypes.c_int64(0)
+        info = c.dbscan_info()
+        st = c.dbscan_graph_device(
+            xt.data_ptr(), n, d, eps, row_ptr.data_ptr(),
+            col.data_ptr() if col is not None else None, cap, nnz,
+            ws.data_ptr(), ws.numel(), stream.cuda_stream, flags, info)
+        return st, nnz.value, info
+
+    ws = torch.empty(c.dbscan_graph_workspace_bytes(n, d, 0), dtype=torch.uint8,
+                     device=xt.device)
+    st, nnz, info = call(ws, None, 0)
+    if st not in (0, c.ERR_CAPACITY):
+        raise apd.DbscanError(st, info.hip_error)
+    pairs_needed = int(info.n_edges)
+    ws = torch.empty(c.dbscan_graph_workspace_bytes(n, d, pairs_needed),
+                     dtype=torch.uint8, device=xt.device)
+    col = torch.empty(max(nnz, 1), dtype=torch.int32, device=xt.device)
+    st, _, info = call(ws, col, nnz)                  # warm-up
+    if st != 0:
+        raise apd.DbscanError(st, info.hip_error)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    infos = []
+    start.record(stream)
+    for _ in range(steps):
+        st, _, info = call(ws, col, nnz)
+        if st != 0:
+            raise apd.DbscanError(st, info.hip_error)
+        infos.append(info)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    parity = "unchecked"
+    if not no_parity and g is not None and "graph_sha256" in g:
+        h = hashlib.sha256()
+        h.update(row_ptr.cpu().numpy().astype("<i8").tobytes())
+        h.update(col[:nnz].cpu().numpy().astype("<i4").tobytes())
+        parity = ("row_ptr+col_idx bit-exact vs oracle"
+                  if h.hexdigest() == g["graph_sha256"] else "MISMATCH vs oracle")
+    mean = lambda f: float(np.mean([getattr(i, f) for i in infos]))
+    return {
+        "what": "sparse eps-graph export (dbscan_graph_device, CSR, rows "
+                "ascending, self included) with the pruned count pass",
+        "ms_per_step": ms,
+        "nnz": nnz,
+        "entries_per_s": nnz / (ms / 1e3),
+        "phases_ms": {"layout_sort_boxes": mean("ms_layout"),
+                      "count": mean("ms_count"),
+                      "row_offsets": mean("ms_core"),
+                      "scatter": mean("ms_merge"),
+                      "row_sort": mean("ms_label")},
+        "parity": parity,
+    }
 
 
 def main():
@@ -249,6 +317,9 @@ def main():
             "tiles_total": p_last.tiles_total,
             "parity": p_parity,
         }
+    if not args.no_graph_line:
+        out["graph_mode"] = graph_leg(apd, torch, xt, n, d, eps, stream,
+                                      args.steps, g, args.no_parity)
     if args.host_entry:
         apd.fit_host(x, eps, min_pts)            # warm-up (allocations)
         t0 = time.perf_counter()

@@ -54,7 +54,10 @@ typedef enum dbscan_status {
   DBSCAN_ERR_OOM = -4,         /* dbscan_fit only: device allocation failed */
   DBSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than
                                   dbscan_workspace_bytes(n, d), or misaligned */
-  DBSCAN_ERR_HIP = -6          /* any other HIP runtime error */
+  DBSCAN_ERR_HIP = -6,         /* any other HIP runtime error */
+  DBSCAN_ERR_CAPACITY = -7     /* dbscan_graph_device only: the caller's
+                                  col_idx buffer is smaller than the graph
+                                  (the call reports the size needed) */
 } dbscan_status;
 
 /* Merge strategies a fit may take (reported in dbscan_info.merge_mode). */
@@ -173,6 +176,41 @@ int dbscan_relabel_device(const int32_t* d_labels, int64_t n, int32_t* d_ids,
                           int32_t* d_sizes, int64_t* n_clusters,
                           void* d_workspace, size_t workspace_bytes,
                           void* hip_stream);
+
+/* Sparse epsilon-graph in CSR form: row i holds every j with
+ * d2(i,j) <= eps2, i itself included, in ascending j, with d2 and eps2
+ * exactly as for a fit.  These are the per-point neighbour lists that Wang
+ * et al. Sec. IV-B keep as the rows of an N x N cluster matrix ("primitive
+ * clusters"), stored here without the zeros; the row lengths are the
+ * neighbour counts of a fit.
+ *   d_points   device, n*d fp32, row-major; read only.
+ *   d_row_ptr  device, n+1 int64; written whenever the count pass ran
+ *              (also on DBSCAN_ERR_CAPACITY and DBSCAN_ERR_WORKSPACE):
+ *              row_ptr[0] = 0, row_ptr[i+1] - row_ptr[i] = count[i],
+ *              row_ptr[n] = nnz.
+ *   d_col_idx  device, col_capacity int32; on success entries
+ *              row_ptr[i] .. row_ptr[i+1]-1 hold row i.  May be NULL when
+ *              col_capacity is 0 (a size query).
+ *   nnz_out    host int64, or NULL: nnz, whenever the count pass ran.
+ *   d_workspace, workspace_bytes  caller-owned device scratch, 256-byte
+ *              aligned, at least dbscan_graph_workspace_bytes(n, d, pairs)
+ *              for the number of neighbour pairs i<j, (nnz - n) / 2.
+ *   flags      DBSCAN_FLAG_PRUNE_TILES and DBSCAN_FLAG_TIME_PHASES; for
+ *              this call ms_core times the row offsets, ms_merge the
+ *              scatter of the pairs and ms_label the row sort.
+ *   info       optional; n_edges = neighbour pairs i<j, edge_capacity =
+ *              pairs the workspace holds, tiles as for a fit.
+ * Returns DBSCAN_ERR_CAPACITY if nnz > col_capacity or nnz >= 2^32 (the
+ * row sort indexes entries with 32 bits), then DBSCAN_ERR_WORKSPACE if the
+ * pairs do not fit the workspace: a second call with the sizes reported
+ * succeeds.  One distance pass per call.  Synchronises hip_stream (twice)
+ * before returning; not capturable into a HIP graph. */
+size_t dbscan_graph_workspace_bytes(int64_t n, int32_t d, int64_t max_pairs);
+int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
+                        int64_t* d_row_ptr, int32_t* d_col_idx,
+                        int64_t col_capacity, int64_t* nnz_out,
+                        void* d_workspace, size_t workspace_bytes,
+                        void* hip_stream, uint32_t flags, dbscan_info* info);
 
 /* Static, never-NULL description of a status code. */
 const char* dbscan_status_string(int status);

@@ -22,7 +22,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("dbscan_fit", "dbscan_fit_device", "dbscan_fit_device_ex",
                  "dbscan_workspace_bytes", "dbscan_workspace_bytes_with_edges",
-                 "dbscan_status_string", "dbscan_abi_version"):
+                 "dbscan_status_string", "dbscan_abi_version",
+                 "dbscan_relabel_device", "dbscan_relabel_workspace_bytes",
+                 "dbscan_graph_device", "dbscan_graph_workspace_bytes"):
         assert want in names
 
 
@@ -75,6 +77,47 @@ def test_workspace_sizes():
     assert apd.dbscan_workspace_bytes_with_edges(5000, 8, -1) == 0
 
 
+def test_graph_workspace_sizes():
+    assert apd.dbscan_graph_workspace_bytes(1000, 0, 10) == 0
+    assert apd.dbscan_graph_workspace_bytes(1000, 3, -1) == 0
+    assert apd.dbscan_graph_workspace_bytes(-1, 3, 10) == 0
+    for n in (0, 1, 5000, 10 ** 6):
+        base = apd.dbscan_workspace_bytes(n, 3)
+        b0 = apd.dbscan_graph_workspace_bytes(n, 3, 0)
+        # the pair area doubles as the row sort's second buffer: at least
+        # 4 bytes per graph entry (n self entries + 2 per pair)
+        assert b0 >= base + 4 * max(n, 1) and b0 % 256 == 0
+        b1 = apd.dbscan_graph_workspace_bytes(n, 3, 1000)
+        assert b1 >= b0 + 8000
+
+
+def _graph_status(x, n, d, eps, row_ptr=True, col=None, cap=0, flags=0,
+                  ws_bytes=16):
+    rp = np.zeros(max(n, 0) + 1, np.int64)
+    ws = np.zeros(ws_bytes, np.uint8)
+    return apd.dbscan_graph_device(
+        x.ctypes.data if x is not None else None, n, d, eps,
+        rp.ctypes.data if row_ptr else None,
+        col.ctypes.data if col is not None else None, cap, None,
+        ws.ctypes.data, ws_bytes, None, flags, None)
+
+
+def test_graph_invalid_arguments_rejected_before_device_work():
+    x = np.zeros((8, 2), np.float32)
+    bad = _capi.ERR_INVALID_ARG
+    assert _graph_status(x, 8, 0, 0.1) == bad
+    assert _graph_status(x, 8, 65, 0.1) == bad
+    assert _graph_status(x, -1, 2, 0.1) == bad
+    assert _graph_status(x, 8, 2, -0.5) == bad
+    assert _graph_status(x, 8, 2, float("nan")) == bad
+    assert _graph_status(None, 8, 2, 0.1) == bad
+    assert _graph_status(x, 8, 2, 0.1, row_ptr=False) == bad
+    assert _graph_status(x, 8, 2, 0.1, cap=-1) == bad
+    assert _graph_status(x, 8, 2, 0.1, cap=10) == bad        # NULL col_idx
+    assert _graph_status(x, 8, 2, 0.1, flags=0x2) == bad      # not for graphs
+    assert _graph_status(x, 8, 2, 0.1, flags=0x80) == bad
+
+
 def _status(points, n, d, eps, m, labels=True):
     lab = np.empty(max(n, 1), np.int32)
     return apd.dbscan_fit(points.ctypes.data if points is not None else None,
@@ -115,3 +158,4 @@ def test_no_device_reported():
     with pytest.raises(apd.DbscanError) as e:
         apd.fit_host(x, 0.1, 1)
     assert e.value.status == _capi.ERR_NO_DEVICE
+    assert _graph_status(x, 8, 2, 0.1) == _capi.ERR_NO_DEVICE
