@@ -15,7 +15,8 @@ import importlib
 import numpy as np
 
 _C_NAMES = {
-    "FLAG_FORCE_TILE_MERGE", "FLAG_PRUNE_TILES", "FLAG_TIME_PHASES", "MAX_D",
+    "FLAG_FORCE_TILE_MERGE", "FLAG_PRUNE_TILES", "FLAG_SCREEN",
+    "FLAG_TIME_PHASES", "MAX_D",
     "MERGE_EDGES",
     "MERGE_NONE", "MERGE_TILES", "dbscan_abi_version", "dbscan_fit",
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_info",

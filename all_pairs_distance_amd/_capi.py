@@ -25,6 +25,7 @@ MERGE_NONE, MERGE_EDGES, MERGE_TILES = 0, 1, 2
 FLAG_TIME_PHASES = 0x1
 FLAG_FORCE_TILE_MERGE = 0x2
 FLAG_PRUNE_TILES = 0x4
+FLAG_SCREEN = 0x8
 MAX_D = 64
 
 

@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libdbscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "k_count.hip", "k_prep.hip", "k_merge.hip",
-           "k_prune.hip", "k_relabel.hip", "k_graph.hip"]
+           "k_prune.hip", "k_relabel.hip", "k_graph.hip",
+           "k_screen.hip"]
 HEADERS = ["internal.h", "device.h"]
 ARCH = "gfx950"
 FLAGS = [

@@ -34,7 +34,7 @@ static int64_t tile_capacity(int64_t n_pad, int D) {
   return all < kTileListCap ? all : kTileListCap;
 }
 
-constexpr int kRegions = 21;
+constexpr int kRegions = 23;
 
 // Region sizes in carve order; every region starts 256-byte aligned.
 static size_t regions(int64_t n_pad, int D, size_t* out) {
@@ -62,6 +62,8 @@ static size_t regions(int64_t n_pad, int D, size_t* out) {
       (size_t)tile_capacity(n_pad, D) * sizeof(uint2),  // tiles
       np / 64 * 2 * S * sizeof(float),                   // boxes64
       np / (64 * (size_t)lane_points(D)) * 2 * S * sizeof(float),  // boxes_w
+      np * (size_t)screen_stride(D) * sizeof(float),  // srow
+      np * sizeof(float),            // ncol
       sort_bytes(n_pad),             // radix sort scratch (last)
   };
   size_t total = 0;
@@ -104,8 +106,10 @@ bool carve(Layout& L, void* ws, size_t ws_bytes) {
   L.tile_cap = (unsigned long long)tile_capacity(L.n_pad, L.D);
   L.boxes64 = reinterpret_cast<float*>(b + off[18]);
   L.boxes_w = reinterpret_cast<float*>(b + off[19]);
-  L.sort_tmp = b + off[20];
-  L.sort_tmp_bytes = need - off[20];
+  L.srow = reinterpret_cast<float*>(b + off[20]);
+  L.ncol = reinterpret_cast<float*>(b + off[21]);
+  L.sort_tmp = b + off[22];
+  L.sort_tmp_bytes = need - off[22];
   L.bytes_min = need;
   const size_t spare = ws_bytes - need;
   L.edges = reinterpret_cast<uint2*>(b + need);
@@ -122,7 +126,8 @@ namespace {
 
 constexpr uint32_t kKnownFlags = DBSCAN_FLAG_TIME_PHASES |
                                   DBSCAN_FLAG_FORCE_TILE_MERGE |
-                                  DBSCAN_FLAG_PRUNE_TILES;
+                                  DBSCAN_FLAG_PRUNE_TILES |
+                                  DBSCAN_FLAG_SCREEN;
 
 int check_args(int64_t n, int32_t d, float eps, int32_t min_pts) {
   if (n < 0 || n > (int64_t)INT32_MAX) return DBSCAN_ERR_INVALID_ARG;
@@ -286,14 +291,17 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   const bool want_edges =
       L.edge_cap > 0 && !(flags & DBSCAN_FLAG_FORCE_TILE_MERGE);
   const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
+  const bool screen = (flags & DBSCAN_FLAG_SCREEN) != 0;
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
   int64_t pass1 = 0, pass2 = 0;
 
   tm.mark(0);
   DB_TRY(launch_prepare(L, d_points, stream));
   if (prune) DB_TRY(launch_prune(L, block_points(L.D), eps2, stream));
+  if (screen)
+    DB_TRY(launch_screen(L, prune ? L.sorted_pts : L.pts, eps2, stream));
   tm.mark(1);
-  DB_TRY(launch_count(L, eps2, want_edges, prune, stream, &pass1));
+  DB_TRY(launch_count(L, eps2, want_edges, prune, screen, stream, &pass1));
   tm.mark(2);
   DB_TRY(launch_core(L, min_pts, d_counts, stream));
 
@@ -439,7 +447,8 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   if (info) std::memset(info, 0, sizeof(*info));
   int st = check_args(n, d, eps, 1);
   if (st != DBSCAN_OK) return st;
-  if (flags & ~(DBSCAN_FLAG_TIME_PHASES | DBSCAN_FLAG_PRUNE_TILES))
+  if (flags & ~(DBSCAN_FLAG_TIME_PHASES | DBSCAN_FLAG_PRUNE_TILES |
+                DBSCAN_FLAG_SCREEN))
     return DBSCAN_ERR_INVALID_ARG;
   if (d_row_ptr == nullptr || col_capacity < 0 ||
       (col_capacity > 0 && d_col_idx == nullptr) ||
@@ -473,6 +482,7 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   volatile float eps_v = eps;
   const float eps2 = eps_v * eps_v;
   const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
+  const bool screen = (flags & DBSCAN_FLAG_SCREEN) != 0;
   const unsigned long long col_cap = (unsigned long long)col_capacity;
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
   int64_t pass1 = 0;
@@ -480,8 +490,10 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   tm.mark(0);
   DB_TRY(launch_prepare(L, d_points, stream));
   if (prune) DB_TRY(launch_prune(L, block_points(L.D), eps2, stream));
+  if (screen)
+    DB_TRY(launch_screen(L, prune ? L.sorted_pts : L.pts, eps2, stream));
   tm.mark(1);
-  DB_TRY(launch_count(L, eps2, true, prune, stream, &pass1));
+  DB_TRY(launch_count(L, eps2, true, prune, screen, stream, &pass1));
   tm.mark(2);
   DB_TRY(launch_row_offsets(L, G, d_row_ptr, d_col_idx, col_cap, stream));
   Status host_st;

@@ -27,7 +27,9 @@ struct Status {
   unsigned int n_core_list;        // entries written by the core compaction
   unsigned int graph_bad;           // a graph slot fell outside its row
   unsigned long long n_tiles;      // block pairs kept by the tile pruning
-  unsigned int pad[8];
+  unsigned long long ymax_bits;    // largest squared norm (fp64 bits), screen
+  unsigned int screen_unsafe;      // a norm too large for the screen bound
+  unsigned int pad[5];
 };
 static_assert(sizeof(Status) == 64, "status block is 64 bytes");
 
@@ -40,6 +42,10 @@ constexpr int row_stride(int D) { return D <= 2 ? D : ((D + 3) & ~3); }
 // (extra coordinates are 0 on both sides, which adds exact zeros to the sum).
 constexpr int kDims[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
 int pick_dim(int d);  // smallest compiled D >= d, or 0
+
+// Row stride of the screen's row table: -2x (D floats), then the two
+// thresholds, padded to a multiple of 4 floats.
+constexpr int screen_stride(int D) { return (D + 2 + 3) & ~3; }
 
 // Column points per lane of the count pass (P) for width D; its blocks hold
 // T = 256 * P points (4 waves of 64 lanes).
@@ -76,6 +82,8 @@ struct Layout {
   float* boxes_w;      // [n_pad/(64P)][2][stride] boxes of a wave's columns
   uint2* tiles;        // kept block pairs
   unsigned long long tile_cap;
+  float* srow;         // [n_pad][screen_stride] screen row table
+  float* ncol;         // [n_pad] fp32 squared norm of each point (screen)
   void* sort_tmp;      // radix sort scratch
   size_t sort_tmp_bytes;
   uint2* edges;        // edge area (may be empty)
@@ -98,7 +106,9 @@ bool carve(Layout& L, void* ws, size_t ws_bytes);
 // ---- launchers (each enqueues on `s` and returns hipGetLastError) -------
 hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s);
 hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
-                        hipStream_t s, int64_t* pairs);
+                        bool screen, hipStream_t s, int64_t* pairs);
+hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
+                         hipStream_t s);
 size_t prune_sort_bytes(int64_t n_pad);
 hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s);
 hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,

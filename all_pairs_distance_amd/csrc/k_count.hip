@@ -27,9 +27,12 @@ namespace dbk {
 
 // Minimum waves per SIMD the register allocator is asked to allow (1 = no
 // constraint), chosen per width by measurement: the narrow widths fit 8
-// waves (<= 64 VGPRs) and run faster there; the wide ones would spill.
-constexpr int count_waves(int D, bool edges) {
-  return D <= 16 ? 8 : 1;
+// waves (<= 64 VGPRs) and run faster there; the wide ones would spill.  The
+// screen keeps one more value per column point (its norm) and its own
+// masks, so it is given more registers.
+constexpr int count_waves(int D, bool edges, bool screen) {
+  return screen ? (D <= 2 ? 4 : D <= 4 ? 5 : D <= 16 ? 6 : 1)
+                : (D <= 2 ? 5 : D <= 16 ? 8 : 1);
 }
 
 // Upper-triangle tile t (row-major over I <= J of nb x nb blocks) -> (I, J).
@@ -98,7 +101,15 @@ __device__ __forceinline__ void stage_edges(uint64_t m, int64_t row,
 // column points.
 // With PRUNED, pts is the sorted copy and perm maps a sorted position to
 // the original index: counts and captured pairs go to original indices.
-template <int D, int P, bool DIAG, bool EDGES, bool PRUNED>
+//
+// With SCREEN, most pairs are decided without the exact distance: a screen
+// value v = |y|^2 - 2 x.y (fused multiply-adds from the column's norm,
+// with the row pre-scaled by -2) is compared with two per-row thresholds
+// that bracket the exact decision by a proven error bound (k_screen.hip).
+// v <= lo: certainly a neighbour; v > hi: certainly not; in between the
+// row's exact distances are evaluated on a rare, wave-uniform path, so the
+// result is bit-identical to the exact pass.
+template <int D, int P, bool DIAG, bool EDGES, bool PRUNED, bool SCREEN>
 __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            int64_t row0, int rows,
                                            int64_t colw, float eps2,
@@ -107,15 +118,20 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            const EdgeSink& sink,
                                            const int* __restrict__ perm,
                                            const float* __restrict__ boxes64,
-                                           const float* __restrict__ boxes_w) {
+                                           const float* __restrict__ boxes_w,
+                                           const float* __restrict__ srow,
+                                           const float* __restrict__ ncol) {
   constexpr int S = row_stride(D);
+  constexpr int SR = screen_stride(D);
   const int lane = lane_id();
   float xc[P][D];
+  float ny[SCREEN ? P : 1];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const float* cp = pts + (colw + p * 64 + lane) * S;
 #pragma unroll
     for (int k = 0; k < D; ++k) xc[p][k] = cp[k];
+    if (SCREEN) ny[p] = ncol[colw + p * 64 + lane];
   }
   unsigned lc[P];
 #pragma unroll
@@ -135,46 +151,93 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 #pragma unroll 1
     for (int l = 0; l < 64; ++l) {
       const int64_t row = row0 + rb + l;
-      // wave-uniform address: read through the constant address space so
-      // the row lands in SGPRs via scalar loads
-      const const_float_ptr rp = (const_float_ptr)(pts + row * S);
-      float xr[D];
+      // one value per column group: the exact distance, or the screen value
+      float val[P];
+      float lo = 0.f, thr = eps2;
+      if (SCREEN) {
+        // wave-uniform address: read through the constant address space so
+        // the row lands in SGPRs via scalar loads
+        const const_float_ptr sp = (const_float_ptr)(srow + row * SR);
+        float a[D];
 #pragma unroll
-      for (int k = 0; k < D; ++k) xr[k] = rp[k];
+        for (int k = 0; k < D; ++k) a[k] = sp[k];
+        lo = sp[D];
+        thr = sp[D + 1];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          float v = ny[p];
+#pragma unroll
+          for (int k = 0; k < D; ++k) v = __builtin_fmaf(a[k], xc[p][k], v);
+          val[p] = v;
+        }
+      } else {
+        const const_float_ptr rp = (const_float_ptr)(pts + row * S);
+        float xr[D];
+#pragma unroll
+        for (int k = 0; k < D; ++k) xr[k] = rp[k];
+#pragma unroll
+        for (int p = 0; p < P; ++p) val[p] = dist2<D>(xr, xc[p]);
+      }
+      // Most rows have no neighbour among these 64*P columns: one compare
+      // of the lane's smallest value settles that for all P groups (min
+      // returns the other operand for a NaN, so padding never hides a
+      // real column), and only rows with a candidate pay for the masks,
+      // the counters and the captured pairs, on one wave-uniform branch.
+      float vmin = val[0];
+#pragma unroll
+      for (int p = 1; p < P; ++p) vmin = __builtin_fminf(vmin, val[p]);
       unsigned acc = 0;
       uint64_t m[P];
+      if (ballot(vmin <= thr)) {
+        if (SCREEN) {
+          uint64_t amb = 0;
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const float s = dist2<D>(xr, xc[p]);
-        const bool nb = s <= eps2;
-        m[p] = ballot(nb);
-        acc += (unsigned)__popcll(m[p]);
-        if (!DIAG) lc[p] = add_lane_bit(lc[p], m[p]);
-      }
-      // the row's count over these columns is 0 for most rows: one
-      // wave-uniform branch per row keeps the P distance chains free of
-      // control flow so they interleave
-      if (EDGES && acc != 0) {
-        int lane_col = (int)(colw + lane);
-        // recomputed here, on the rare path, instead of P live registers
-        asm volatile("" : "+v"(lane_col));
-        const int row_out = PRUNED ? ((const_int_ptr)perm)[row] : (int)row;
-        // at most 8 column groups (512 pairs) are staged per capacity check
-#pragma unroll
-        for (int g = 0; g < P; g += 8) {
-          constexpr int G = P < 8 ? P : 8;
-          unsigned want = 0;
-#pragma unroll
-          for (int p = g; p < g + G; ++p) want += (unsigned)__popcll(m[p]);
-          if (fill + want > (unsigned)kEdgeStage) {
-            flush_edges(stage, fill, sink);
-            fill = 0;
+          for (int p = 0; p < P; ++p) {
+            m[p] = ballot(val[p] <= lo);
+            amb |= ballot(val[p] <= thr) & ~m[p];
           }
+          if (amb) {
+            // some pair of this row lies inside the bound: decide the
+            // row's pairs with the exact distance
+            const const_float_ptr rp = (const_float_ptr)(pts + row * S);
+            float xr[D];
 #pragma unroll
-          for (int p = g; p < g + G; ++p) {
-            const int col = lane_col + p * 64;
-            stage_edges<DIAG>(m[p], row, colw + p * 64, row_out,
-                              PRUNED ? perm[col] : col, stage, fill);
+            for (int k = 0; k < D; ++k) xr[k] = rp[k];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+              m[p] = ballot(dist2<D>(xr, xc[p]) <= eps2);
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < P; ++p) m[p] = ballot(val[p] <= eps2);
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          acc += (unsigned)__popcll(m[p]);
+          if (!DIAG) lc[p] = add_lane_bit(lc[p], m[p]);
+        }
+        if (EDGES && acc != 0) {
+          int lane_col = (int)(colw + lane);
+          // recomputed here, on the rare path, instead of P live registers
+          asm volatile("" : "+v"(lane_col));
+          const int row_out = PRUNED ? ((const_int_ptr)perm)[row] : (int)row;
+          // at most 8 column groups (512 pairs) staged per capacity check
+#pragma unroll
+          for (int g = 0; g < P; g += 8) {
+            constexpr int G = P < 8 ? P : 8;
+            unsigned want = 0;
+#pragma unroll
+            for (int p = g; p < g + G; ++p) want += (unsigned)__popcll(m[p]);
+            if (fill + want > (unsigned)kEdgeStage) {
+              flush_edges(stage, fill, sink);
+              fill = 0;
+            }
+#pragma unroll
+            for (int p = g; p < g + G; ++p) {
+              const int col = lane_col + p * 64;
+              stage_edges<DIAG>(m[p], row, colw + p * 64, row_out,
+                                PRUNED ? perm[col] : col, stage, fill);
+            }
           }
         }
       }
@@ -195,16 +258,17 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
   }
 }
 
-template <int D, bool EDGES, bool PRUNED>
+template <int D, bool EDGES, bool PRUNED, bool SCREEN>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES), 8))) void k_count(
+__attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_count(
     const float* __restrict__ pts, int64_t nb, int chunks_log2, int rows,
     int64_t items, float eps2, unsigned* __restrict__ count,
     uint2* __restrict__ edges, unsigned long long cap,
     unsigned long long* __restrict__ counter,
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
     unsigned long long tile_cap, const int* __restrict__ perm,
-    const float* __restrict__ boxes64, const float* __restrict__ boxes_w) {
+    const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
+    const float* __restrict__ srow, const float* __restrict__ ncol) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
@@ -236,20 +300,21 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES), 8))) void k_count(
     const int64_t row0 = I * T + (int64_t)c * rows;
     const int64_t colw = J * T + (int64_t)wave * 64 * P;
     if (I == J)
-      count_item<D, P, true, EDGES, PRUNED>(pts, row0, rows, colw, eps2, count,
-                                            stage, fill, sink, perm, boxes64,
-                                            boxes_w);
+      count_item<D, P, true, EDGES, PRUNED, SCREEN>(
+          pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
+          boxes_w, srow, ncol);
     else
-      count_item<D, P, false, EDGES, PRUNED>(pts, row0, rows, colw, eps2,
-                                             count, stage, fill, sink, perm,
-                                             boxes64, boxes_w);
+      count_item<D, P, false, EDGES, PRUNED, SCREEN>(
+          pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
+          boxes_w, srow, ncol);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
 
 template <int D>
 static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
-                                 bool pruned, hipStream_t s, int64_t* pairs) {
+                                 bool pruned, bool screen, hipStream_t s,
+                                 int64_t* pairs) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   const int64_t nb = L.n_pad / T;
@@ -271,25 +336,31 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   pts, nb, chunks_log2, rows, items, eps2, L.count,                         \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
-      L.boxes_w
-  if (edges && pruned)
-    k_count<D, true, true><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
-  else if (edges)
-    k_count<D, true, false><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
-  else if (pruned)
-    k_count<D, false, true><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
-  else
-    k_count<D, false, false><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS);
+      L.boxes_w, L.srow, L.ncol
+#define DBK_LAUNCH(E, PR, SC) \
+  k_count<D, E, PR, SC><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS)
+  if (screen) {
+    if (edges && pruned) DBK_LAUNCH(true, true, true);
+    else if (edges) DBK_LAUNCH(true, false, true);
+    else if (pruned) DBK_LAUNCH(false, true, true);
+    else DBK_LAUNCH(false, false, true);
+  } else {
+    if (edges && pruned) DBK_LAUNCH(true, true, false);
+    else if (edges) DBK_LAUNCH(true, false, false);
+    else if (pruned) DBK_LAUNCH(false, true, false);
+    else DBK_LAUNCH(false, false, false);
+  }
+#undef DBK_LAUNCH
 #undef DBK_COUNT_ARGS
   if (pairs) *pairs = L.n_pad * L.n_pad;
   return hipGetLastError();
 }
 
 hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
-                        hipStream_t s, int64_t* pairs) {
+                        bool screen, hipStream_t s, int64_t* pairs) {
   switch (L.D) {
 #define DBK_CASE(DD) \
-  case DD: return launch_count_d<DD>(L, eps2, edges, pruned, s, pairs);
+  case DD: return launch_count_d<DD>(L, eps2, edges, pruned, screen, s, pairs);
     DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
     DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)
     DBK_CASE(64)

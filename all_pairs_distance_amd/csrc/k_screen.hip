@@ -1,0 +1,147 @@
+// Screen tables for the count pass (an opt-in mode).
+//
+// The exact decision is D(x,y) <= eps2 with D the fp32 direct distance
+// (ascending k, every operation rounded).  Wang et al. (Sec. IV-B2) hoist
+// the squared norms out of the distance, T + P - 2 t.p; here that form is
+// only a screen: the count pass computes
+//     v = fl-chain of fused multiply-adds  n_y + sum_k (-2 x_k) * y_k
+// with n_y = fl32(|y|^2), which approximates R - |x|^2, R = |x - y|^2 the
+// real squared distance, and compares it with two per-row thresholds.
+//
+// Bounds (u = 2^-24, g_m = m u / (1 - m u), t = 2^-149):
+//   direct:  R (1 - g_{D+2}) - (D+2) t <= D(x,y) <= R (1 + g_{D+2}) + (D+2) t
+//            (d+2 roundings per term; a subnormal result of a subtraction is
+//            exact, of a product or sum off by at most t/2)
+//   screen:  |v - (R - |x|^2)| <= k (|x|^2 + |y|^2) + (D+1) t,
+//            k = u + 2.01 g_D  (n_y rounded once; D fused steps each rounded
+//            once, the partial sums bounded by |y|^2 + sum |2 x_k y_k|
+//            <= 2|y|^2 + |x|^2)
+// With L = (eps2 - (D+2) t) / (1 + g_{D+2}) and
+//      H = (eps2 + (D+2) t) / (1 - g_{D+2}):
+//   R <= L  implies D <= eps2;   R > H  implies D > eps2.
+// Bounding |y|^2 by the largest squared norm Y of the set, each row x gets
+//   lo = RD(L - |x|^2 - m(x)),  hi = RU(H - |x|^2 + m(x)),
+//   m(x) = k (|x|^2 + Y) + (D+1) t  (+ 1e-12 of the magnitudes for the fp64
+//          evaluation of these expressions),
+// rounded down / up to fp32.  Then v <= lo proves R <= L (a neighbour) and
+// v > hi proves R > H (not one); anything else is decided exactly.  |x|^2 is
+// summed in fp64 from exact fp64 squares.  If any squared norm exceeds
+// 2^100 (where products could overflow) every row gets lo = -inf,
+// hi = +inf and zero coefficients: all pairs are then decided exactly.
+// Padding rows are NaN throughout and never match.
+#include <cmath>
+
+#include "device.h"
+#include "internal.h"
+
+namespace dbk {
+
+static unsigned grid_for_s(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (unsigned)(g < kMaxGrid ? g : kMaxGrid);
+}
+
+__device__ __forceinline__ double sq_norm64(const float* __restrict__ p, int S) {
+  double s = 0.0;
+  for (int k = 0; k < S; ++k) {
+    const double x = (double)p[k];
+    s += x * x;   // fp64 product of an fp32 value: exact
+  }
+  return s;
+}
+
+// Pass 1: fp32 norms of every point and the largest fp64 squared norm.
+__global__ __launch_bounds__(256) void k_screen_norms(
+    const float* __restrict__ pts, int64_t n_pad, int S,
+    float* __restrict__ ncol, Status* __restrict__ st) {
+  double ymax = 0.0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const double s = sq_norm64(pts + i * S, S);
+    if (s == s) {                    // real point (padding rows are NaN)
+      ncol[i] = (float)s;            // round to nearest
+      ymax = s > ymax ? s : ymax;
+    } else {
+      ncol[i] = __builtin_nanf("");
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const double o = __shfl_xor(ymax, off);
+    ymax = o > ymax ? o : ymax;
+  }
+  if (lane_id() == 0 && ymax > 0.0) {
+    // non-negative doubles order like their bit patterns
+    atomicMax(&st->ymax_bits, (unsigned long long)__double_as_longlong(ymax));
+    if (!(ymax <= 0x1p100)) atomicOr(&st->screen_unsafe, 1u);
+  }
+}
+
+// Pass 2: the row table: -2 x_k, then lo and hi.
+template <int D>
+__global__ __launch_bounds__(256) void k_screen_rows(
+    const float* __restrict__ pts, int64_t n_pad, float eps2,
+    float* __restrict__ srow, float* __restrict__ ncol,
+    const Status* __restrict__ st) {
+  constexpr int S = row_stride(D);
+  constexpr int SR = screen_stride(D);
+  const double u = 0x1p-24, t = 0x1p-149;
+  const double gD = D * u / (1.0 - D * u);
+  const double g2 = (D + 2) * u / (1.0 - (D + 2) * u);
+  const double kap = u + 2.01 * gD;
+  const double e2 = (double)eps2;
+  const double L = (e2 - (D + 2) * t) / (1.0 + g2);
+  const double H = (e2 + (D + 2) * t) / (1.0 - g2);
+  const double Y = __longlong_as_double((long long)st->ymax_bits);
+  const bool unsafe = st->screen_unsafe != 0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float* p = pts + i * S;
+    float* out = srow + i * SR;
+    const double x2 = sq_norm64(p, S);
+    if (!(x2 == x2)) {               // padding row
+      for (int k = 0; k < SR; ++k) out[k] = __builtin_nanf("");
+      continue;
+    }
+    if (unsafe) {
+      for (int k = 0; k < D; ++k) out[k] = 0.f;
+      out[D] = -__builtin_inff();
+      out[D + 1] = __builtin_inff();
+      ncol[i] = 0.f;
+    } else {
+      for (int k = 0; k < D; ++k) out[k] = -2.f * p[k];   // exact
+      if (!(e2 < 0x1p128)) {         // eps2 = +inf: every pair is a neighbour
+        out[D] = __builtin_inff();
+        out[D + 1] = __builtin_inff();
+      } else {
+        const double m = kap * (x2 + Y) + (D + 1) * t +
+                         1e-12 * (fabs(L) + fabs(H) + x2 + Y);
+        out[D] = __double2float_rd(L - x2 - m);
+        out[D + 1] = __double2float_ru(H - x2 + m);
+      }
+    }
+    for (int k = D + 2; k < SR; ++k) out[k] = 0.f;
+  }
+}
+
+hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
+                         hipStream_t s) {
+  k_screen_norms<<<grid_for_s(L.n_pad, 256 * 4), 256, 0, s>>>(
+      pts, L.n_pad, L.stride, L.ncol, L.status);
+  const unsigned grid = grid_for_s(L.n_pad, 256 * 4);
+  switch (L.D) {
+#define DBK_CASE(DD)                                                       \
+  case DD:                                                                 \
+    k_screen_rows<DD><<<grid, 256, 0, s>>>(pts, L.n_pad, eps2, L.srow,     \
+                                           L.ncol, L.status);              \
+    break;
+    DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
+    DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)
+    DBK_CASE(64)
+#undef DBK_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dbk

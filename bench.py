@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--prune", action="store_true",
                     help="time the exact tile-pruned fit as the main line")
+    ap.add_argument("--screen", action="store_true",
+                    help="time the screened count pass as the main line")
+    ap.add_argument("--no-screen-line", action="store_true",
+                    help="skip the screen_mode measurements")
     ap.add_argument("--no-graph-line", action="store_true",
                     help="skip the sparse eps-graph export leg")
     ap.add_argument("--no-pruned-line", action="store_true",
@@ -204,7 +208,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     flags = (apd.FLAG_TIME_PHASES
              | (apd.FLAG_FORCE_TILE_MERGE if args.tile_merge else 0)
-             | (apd.FLAG_PRUNE_TILES if args.prune else 0))
+             | (apd.FLAG_PRUNE_TILES if args.prune else 0)
+             | (apd.FLAG_SCREEN if args.screen else 0))
 
     def step(fl):
         info = apd.dbscan_info()
@@ -296,27 +301,41 @@ def main():
     }
     out["config"]["tiles_kept"] = last.tiles_kept
     out["config"]["tiles_total"] = last.tiles_total
-    if not args.prune and not args.no_pruned_line:
-        p_infos, p_ms, _ = timed(flags | apd.FLAG_PRUNE_TILES, args.steps, 1)
-        p_last = p_infos[-1]
-        p_parity = "unchecked"
+    def mode_leg(fl, what):
+        m_infos, m_ms, _ = timed(fl, args.steps, 1)
+        m_last = m_infos[-1]
+        m_parity = "unchecked"
         if not args.no_parity and parity != "unchecked":
             ok = (digest(labels.cpu().numpy()) == g["labels_sha256"]
                   and digest(counts.cpu().numpy()) == g["counts_sha256"])
-            p_parity = "labels+counts bit-exact vs oracle" if ok else "MISMATCH vs oracle"
-        out["pruned_mode"] = {
-            "what": "same fit with exact tile pruning (DBSCAN_FLAG_PRUNE_TILES): "
-                    "block pairs whose fp32 box-gap bound exceeds eps^2 are "
-                    "skipped, every pair is still decided",
-            "value": pairs / (p_ms / 1e3),
+            m_parity = "labels+counts bit-exact vs oracle" if ok else "MISMATCH vs oracle"
+        return {
+            "what": what,
+            "value": pairs / (m_ms / 1e3),
             "unit": "pair relations decided/s",
-            "ms_per_step": p_ms,
-            "ms_count": float(np.mean([i.ms_count for i in p_infos])),
-            "ms_layout_sort_boxes": float(np.mean([i.ms_layout for i in p_infos])),
-            "tiles_kept": p_last.tiles_kept,
-            "tiles_total": p_last.tiles_total,
-            "parity": p_parity,
+            "ms_per_step": m_ms,
+            "ms_count": float(np.mean([i.ms_count for i in m_infos])),
+            "ms_layout_sort_boxes": float(np.mean([i.ms_layout for i in m_infos])),
+            "tiles_kept": m_last.tiles_kept,
+            "tiles_total": m_last.tiles_total,
+            "parity": m_parity,
         }
+
+    if not args.prune and not args.no_pruned_line:
+        out["pruned_mode"] = mode_leg(
+            flags | apd.FLAG_PRUNE_TILES,
+            "same fit with exact tile pruning (DBSCAN_FLAG_PRUNE_TILES): "
+            "block pairs whose fp32 box-gap bound exceeds eps^2 are "
+            "skipped, every pair is still decided")
+    if not args.screen and not args.no_screen_line:
+        out["screen_mode"] = mode_leg(
+            flags | apd.FLAG_SCREEN,
+            "same fit with the screened count pass (DBSCAN_FLAG_SCREEN): "
+            "hoisted-norm screen with a proven error bound, exact distance "
+            "for the undecided pairs; identical results")
+        out["pruned_screen_mode"] = mode_leg(
+            flags | apd.FLAG_SCREEN | apd.FLAG_PRUNE_TILES,
+            "tile pruning and the screened count pass together")
     if not args.no_graph_line:
         out["graph_mode"] = graph_leg(apd, torch, xt, n, d, eps, stream,
                                       args.steps, g, args.no_parity)

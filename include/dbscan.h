@@ -85,6 +85,17 @@ typedef enum dbscan_status {
                                         arithmetic); results are identical,
                                         far fewer distances are evaluated
                                         when d is small */
+#define DBSCAN_FLAG_SCREEN 0x8u /* decide most pairs of the count pass with
+                                   the hoisted-norm form |y|^2 - 2 x.y
+                                   (Wang et al. Sec. IV-B2) evaluated with
+                                   fused multiply-adds, against per-point
+                                   thresholds that bracket the exact
+                                   decision by a proven rounding-error
+                                   bound; pairs inside the bracket are
+                                   decided with the exact distance, so the
+                                   results are identical to the exact pass
+                                   and about d instead of 3d operations are
+                                   spent per pair */
 
 /* What a fit did; filled by dbscan_fit_device_ex when info != NULL. */
 typedef struct dbscan_info {
@@ -195,7 +206,8 @@ int dbscan_relabel_device(const int32_t* d_labels, int64_t n, int32_t* d_ids,
  *   d_workspace, workspace_bytes  caller-owned device scratch, 256-byte
  *              aligned, at least dbscan_graph_workspace_bytes(n, d, pairs)
  *              for the number of neighbour pairs i<j, (nnz - n) / 2.
- *   flags      DBSCAN_FLAG_PRUNE_TILES and DBSCAN_FLAG_TIME_PHASES; for
+ *   flags      DBSCAN_FLAG_PRUNE_TILES, DBSCAN_FLAG_SCREEN and
+ *              DBSCAN_FLAG_TIME_PHASES; for
  *              this call ms_core times the row offsets, ms_merge the
  *              scatter of the pairs and ms_label the row sort.
  *   info       optional; n_edges = neighbour pairs i<j, edge_capacity =

@@ -54,7 +54,7 @@ def assert_same_graph(got, want, what):
     assert bad.size == 0, f"{what}: {bad.size} column entries differ, first {bad[:5]}"
 
 
-MODES = [(0, "all_tiles"), (4, "pruned")]
+MODES = [(0, "all_tiles"), (4, "pruned"), (8, "screen"), (12, "pruned_screen")]
 
 
 def test_graph_handworked(apd):

@@ -51,8 +51,9 @@ def assert_same(got_l, got_c, want_l, want_c, what):
     assert bad_l.size == 0, f"{what}: {bad_l.size} labels differ, first {bad_l[:5]}"
 
 
-# 2 = FLAG_FORCE_TILE_MERGE, 4 = FLAG_PRUNE_TILES
-MODES = [(0, "edges"), (2, "tiles"), (4, "pruned"), (6, "pruned_tiles")]
+# 2 = FLAG_FORCE_TILE_MERGE, 4 = FLAG_PRUNE_TILES, 8 = FLAG_SCREEN
+MODES = [(0, "edges"), (2, "tiles"), (4, "pruned"), (6, "pruned_tiles"),
+         (8, "screen"), (12, "pruned_screen"), (10, "screen_tiles")]
 
 
 @pytest.mark.parametrize("flags,mode", MODES, ids=[m for _, m in MODES])
@@ -99,6 +100,10 @@ def test_every_dimension(apd, orc):
         assert_same(lab, cnt, want_l, want_c, f"d={d}")
         lab, cnt, _ = gpu_fit(apd, x, eps, 5, flags=4)
         assert_same(lab, cnt, want_l, want_c, f"d={d} pruned")
+        lab, cnt, _ = gpu_fit(apd, x, eps, 5, flags=8)
+        assert_same(lab, cnt, want_l, want_c, f"d={d} screen")
+        lab, cnt, _ = gpu_fit(apd, x, eps, 5, flags=12)
+        assert_same(lab, cnt, want_l, want_c, f"d={d} pruned screen")
 
 
 def test_pruning_skips_tiles_exactly(apd, orc):
@@ -243,13 +248,17 @@ def _digest(a):
     return hashlib.sha256(np.ascontiguousarray(a.astype("<i4")).tobytes()).hexdigest()
 
 
-@pytest.mark.parametrize("prune", [False, True], ids=["all_tiles", "pruned"])
+NAMED_MODES = [(0, "all_tiles"), (4, "pruned"), (8, "screen"),
+               (12, "pruned_screen")]
+
+
+@pytest.mark.parametrize("flags,mode", NAMED_MODES,
+                         ids=[m for _, m in NAMED_MODES])
 @pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
-def test_named_workload(apd, orc, key, prune):
+def test_named_workload(apd, orc, key, flags, mode):
     x, eps, m, w = datagen.make_workload(key)
-    print(f"workload {key} {w.name} prune={prune}", flush=True)
-    lab, cnt, info = gpu_fit(apd, x, eps, m, max_edges=1 << 30,
-                             flags=4 if prune else 0)
+    print(f"workload {key} {w.name} {mode}", flush=True)
+    lab, cnt, info = gpu_fit(apd, x, eps, m, max_edges=1 << 30, flags=flags)
     assert info["merge_mode"] == 1
     g = _golden().get(str(key))
     if g is not None and g["points_sha256"] == datagen.sha256_points(x):
@@ -295,6 +304,45 @@ def test_named_workload_tile_merge(apd, key):
     b = gpu_fit(apd, x, eps, m, flags=2)
     assert b[2]["merge_mode"] == 2 and b[2]["pass2_pairs"] > 0
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _screen_cases():
+    """Inputs that push the screened count pass onto its exact path: data
+    far from the origin (a wide bound), ties exactly at the radius away
+    from the origin, norms too large for the bound, subnormal scales,
+    duplicates with eps = 0, and an eps whose square overflows."""
+    rng = np.random.default_rng(77)
+    out = []
+    blobs = datagen.gaussian_blobs(3000, 3, seed=71, n_blobs=6, sigma=0.02,
+                                   noise_frac=0.1)
+    out.append(("far_from_origin", (blobs + np.float32(1000.0)).astype(np.float32), 0.03))
+    out.append(("offset_1e6", (blobs + np.float32(1e6)).astype(np.float32), 0.5))
+    lat = datagen.integer_lattice(40, 3).astype(np.float32)
+    out.append(("lattice_ties_offset", (lat + np.float32(37.0)).astype(np.float32), 1.0))
+    out.append(("lattice_ties_diag", (lat * np.float32(0.25) - np.float32(3.0)).astype(np.float32),
+                float(np.sqrt(np.float32(0.125)))))
+    huge = datagen.uniform_points(2000, 4, 5) * np.float32(2.0 ** 60)
+    out.append(("huge_norms", huge.astype(np.float32), float(2.0 ** 57)))
+    tiny = datagen.uniform_points(2000, 2, 6) * np.float32(1e-38)
+    out.append(("subnormal_scale", tiny.astype(np.float32), 2e-40))
+    base = datagen.uniform_points(300, 8, 7)
+    dup = np.ascontiguousarray(base[rng.integers(0, 300, 2500)])
+    out.append(("duplicates_eps0", dup, 0.0))
+    out.append(("eps_square_overflows", datagen.uniform_points(1500, 2, 8), 3e19))
+    wide = datagen.gaussian_blobs(2500, 64, seed=72, n_blobs=5, sigma=0.05,
+                                  noise_frac=0.1)
+    out.append(("d64_offset", (wide + np.float32(20.0)).astype(np.float32), 0.4))
+    return out
+
+
+@pytest.mark.parametrize("flags,mode", [(8, "screen"), (12, "pruned_screen")],
+                         ids=["screen", "pruned_screen"])
+def test_screen_edge_cases(apd, orc, flags, mode):
+    for name, x, eps in _screen_cases():
+        for m in (1, 4):
+            want_l, want_c, _ = orc.fit(x, eps, m)
+            lab, cnt, _ = gpu_fit(apd, x, eps, m, flags=flags)
+            assert_same(lab, cnt, want_l, want_c, f"{name} m={m}")
 
 
 def test_relabel_contiguous(apd, orc):

@@ -40,13 +40,39 @@ def asm(tmp_path_factory):
     }
 
 
+def _screened(name):
+    # k_count<D, EDGES, PRUNED, SCREEN>: the last template flag
+    return re.search(r"ELb[01]ELb[01]ELb1E", name) is not None
+
+
 def test_count_kernels_have_no_fused_or_packed_fp32(asm):
     bodies = kernel_bodies(asm["count"], "k_count")
-    assert len(bodies) == 48   # 12 widths x (edges or not) x (pruned or not)
-    for name, body in bodies.items():
+    # 12 widths x (edges or not) x (pruned or not) x (screened or not)
+    assert len(bodies) == 96
+    exact = {k: v for k, v in bodies.items() if not _screened(k)}
+    assert len(exact) == 48
+    for name, body in exact.items():
         bad = FORBIDDEN.findall(body)
         assert not bad, (name, bad[:3])
         assert "v_sub_f32" in body and "v_mul_f32" in body
+
+
+SCREEN_ALLOWED = re.compile(r"\bv_(fma|fmac)_f32\b")
+
+
+def test_screened_count_kernels(asm):
+    """Screened kernels use fused multiply-adds for the screen value only;
+    packed fp32 never appears, and the exact distance (separate subtract,
+    multiply and add) is still there for the undecided pairs."""
+    bodies = {k: v for k, v in kernel_bodies(asm["count"], "k_count").items()
+              if _screened(k)}
+    assert len(bodies) == 48
+    other = re.compile(r"\b(v_pk_(fma|mul|add)_f32|v_fma_mix\w*|v_(mad|mac)_f32|"
+                       r"v_mad_legacy_f32|v_fmac_legacy_f32|v_dot\w*)\b")
+    for name, body in bodies.items():
+        assert not other.search(body), name
+        assert SCREEN_ALLOWED.search(body), name
+        assert "v_sub_f32" in body and "v_mul_f32" in body, name
 
 
 def test_tile_merge_kernels_have_no_fused_or_packed_fp32(asm):
@@ -57,7 +83,7 @@ def test_tile_merge_kernels_have_no_fused_or_packed_fp32(asm):
 
 
 def test_rows_are_scalar_loads(asm):
-    bodies = kernel_bodies(asm["count"], "k_countILi3ELb0ELb0")
+    bodies = kernel_bodies(asm["count"], "k_countILi3ELb0ELb0ELb0")
     (body,) = bodies.values()
     assert re.search(r"s_load_dword", body)
     # the distance takes its row operand straight from an SGPR
