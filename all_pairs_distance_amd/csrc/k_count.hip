@@ -133,6 +133,14 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
     for (int k = 0; k < D; ++k) xc[p][k] = cp[k];
     if (SCREEN) ny[p] = ncol[colw + p * 64 + lane];
   }
+  // wait for the column loads here, once: otherwise a wait for each group
+  // is re-issued on every row of the loops below
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) asm volatile("" : "+v"(xc[p][k]));
+    if (SCREEN) asm volatile("" : "+v"(ny[p]));
+  }
   unsigned lc[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) lc[p] = 0;
@@ -148,16 +156,21 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                        eps2))
       continue;
     int rowv = 0;  // lane l: count of row rb+l over these columns
-#pragma unroll 1
+    // row addresses advance by a constant per row (the screen's exact path
+    // recomputes its point address instead of carrying a second pointer)
+    const float* next = SCREEN ? srow + (row0 + rb) * SR : pts + (row0 + rb) * S;
+#pragma unroll 2
     for (int l = 0; l < 64; ++l) {
       const int64_t row = row0 + rb + l;
+      const float* cur = next;
+      next += SCREEN ? SR : S;
       // one value per column group: the exact distance, or the screen value
       float val[P];
       float lo = 0.f, thr = eps2;
       if (SCREEN) {
         // wave-uniform address: read through the constant address space so
         // the row lands in SGPRs via scalar loads
-        const const_float_ptr sp = (const_float_ptr)(srow + row * SR);
+        const const_float_ptr sp = (const_float_ptr)cur;
         float a[D];
 #pragma unroll
         for (int k = 0; k < D; ++k) a[k] = sp[k];
@@ -171,7 +184,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
           val[p] = v;
         }
       } else {
-        const const_float_ptr rp = (const_float_ptr)(pts + row * S);
+        const const_float_ptr rp = (const_float_ptr)cur;
         float xr[D];
 #pragma unroll
         for (int k = 0; k < D; ++k) xr[k] = rp[k];
