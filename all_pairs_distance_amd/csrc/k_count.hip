@@ -332,10 +332,12 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   constexpr int T = 256 * P;
   const int64_t nb = L.n_pad / T;
   const int64_t tiles = nb * (nb + 1) / 2;
-  // rows per work item: up to kRowsPerItem, fewer (down to one wave's 64)
-  // while the full triangle would give under 4096 work items (a pruned
-  // launch keeps some of them; how many is only known on the device)
-  int rows = kRowsPerItem < T ? kRowsPerItem : T;
+  // rows per work item: a whole block of T rows, so each column block is
+  // loaded once per tile (a pruned launch keeps only some tiles and splits
+  // them into items of up to kRowsPerItem rows for parallelism); fewer,
+  // down to one wave's 64, while the full triangle would give under 4096
+  // work items
+  int rows = pruned && kRowsPerItem < T ? kRowsPerItem : T;
   while (rows > 64 && tiles * (T / rows) < 4096) rows >>= 1;
   const int chunks = T / rows;  // both powers of two
   int chunks_log2 = 0;
