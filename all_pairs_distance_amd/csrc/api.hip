@@ -127,7 +127,8 @@ namespace {
 constexpr uint32_t kKnownFlags = DBSCAN_FLAG_TIME_PHASES |
                                   DBSCAN_FLAG_FORCE_TILE_MERGE |
                                   DBSCAN_FLAG_PRUNE_TILES |
-                                  DBSCAN_FLAG_SCREEN;
+                                  DBSCAN_FLAG_SCREEN |
+                                  DBSCAN_FLAG_REVERSE_SCHEDULE;
 
 int check_args(int64_t n, int32_t d, float eps, int32_t min_pts) {
   if (n < 0 || n > (int64_t)INT32_MAX) return DBSCAN_ERR_INVALID_ARG;
@@ -292,6 +293,7 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
       L.edge_cap > 0 && !(flags & DBSCAN_FLAG_FORCE_TILE_MERGE);
   const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
   const bool screen = (flags & DBSCAN_FLAG_SCREEN) != 0;
+  const bool reverse = (flags & DBSCAN_FLAG_REVERSE_SCHEDULE) != 0;
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
   int64_t pass1 = 0, pass2 = 0;
 
@@ -301,7 +303,8 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   if (screen)
     DB_TRY(launch_screen(L, prune ? L.sorted_pts : L.pts, eps2, stream));
   tm.mark(1);
-  DB_TRY(launch_count(L, eps2, want_edges, prune, screen, stream, &pass1));
+  DB_TRY(launch_count(L, eps2, want_edges, prune, screen, reverse, stream,
+                      &pass1));
   tm.mark(2);
   DB_TRY(launch_core(L, min_pts, d_counts, stream));
 
@@ -325,9 +328,9 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   tm.mark(3);
   if (n_core > 0) {
     if (edges_ok)
-      DB_TRY(launch_merge_edges(L, host_st.n_edges, stream));
+      DB_TRY(launch_merge_edges(L, host_st.n_edges, reverse, stream));
     else
-      DB_TRY(launch_merge_tiles(L, eps2, n_core, stream, &pass2));
+      DB_TRY(launch_merge_tiles(L, eps2, n_core, reverse, stream, &pass2));
   }
   tm.mark(4);
   DB_TRY(launch_label(L, d_labels, stream));
@@ -493,7 +496,7 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   if (screen)
     DB_TRY(launch_screen(L, prune ? L.sorted_pts : L.pts, eps2, stream));
   tm.mark(1);
-  DB_TRY(launch_count(L, eps2, true, prune, screen, stream, &pass1));
+  DB_TRY(launch_count(L, eps2, true, prune, screen, false, stream, &pass1));
   tm.mark(2);
   DB_TRY(launch_row_offsets(L, G, d_row_ptr, d_col_idx, col_cap, stream));
   Status host_st;

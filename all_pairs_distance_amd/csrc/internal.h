@@ -106,7 +106,8 @@ bool carve(Layout& L, void* ws, size_t ws_bytes);
 // ---- launchers (each enqueues on `s` and returns hipGetLastError) -------
 hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s);
 hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
-                        bool screen, hipStream_t s, int64_t* pairs);
+                        bool screen, bool reverse, hipStream_t s,
+                        int64_t* pairs);
 hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
                          hipStream_t s);
 size_t prune_sort_bytes(int64_t n_pad);
@@ -115,9 +116,9 @@ hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
                        hipStream_t s);
 hipError_t launch_compact(const Layout& L, hipStream_t s);
 hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
-                              hipStream_t s);
+                              bool reverse, hipStream_t s);
 hipError_t launch_merge_tiles(const Layout& L, float eps2, int64_t n_core,
-                              hipStream_t s, int64_t* pairs);
+                              bool reverse, hipStream_t s, int64_t* pairs);
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);
 size_t graph_sort_bytes(int64_t n);
 hipError_t launch_row_offsets(const Layout& L, const GraphLayout& G,

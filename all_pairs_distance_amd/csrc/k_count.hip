@@ -281,7 +281,8 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
     unsigned long long tile_cap, const int* __restrict__ perm,
     const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
-    const float* __restrict__ srow, const float* __restrict__ ncol) {
+    const float* __restrict__ srow, const float* __restrict__ ncol,
+    int reverse) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
@@ -299,7 +300,9 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
       from_list = true;
     }
   }
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+  for (int64_t step = blockIdx.x; step < items; step += gridDim.x) {
+    // (a test mode walks the items in reverse: results must not change)
+    const int64_t item = reverse ? items - 1 - step : step;
     const int64_t tile = item >> chunks_log2;
     const int c = (int)(item & ((1 << chunks_log2) - 1));
     int64_t I, J;
@@ -326,8 +329,8 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
 
 template <int D>
 static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
-                                 bool pruned, bool screen, hipStream_t s,
-                                 int64_t* pairs) {
+                                 bool pruned, bool screen, bool reverse,
+                                 hipStream_t s, int64_t* pairs) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   const int64_t nb = L.n_pad / T;
@@ -351,7 +354,7 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   pts, nb, chunks_log2, rows, items, eps2, L.count,                         \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
-      L.boxes_w, L.srow, L.ncol
+      L.boxes_w, L.srow, L.ncol, reverse ? 1 : 0
 #define DBK_LAUNCH(E, PR, SC) \
   k_count<D, E, PR, SC><<<grid, kThreads, 0, s>>>(DBK_COUNT_ARGS)
   if (screen) {
@@ -372,10 +375,13 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
 }
 
 hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
-                        bool screen, hipStream_t s, int64_t* pairs) {
+                        bool screen, bool reverse, hipStream_t s,
+                        int64_t* pairs) {
   switch (L.D) {
-#define DBK_CASE(DD) \
-  case DD: return launch_count_d<DD>(L, eps2, edges, pruned, screen, s, pairs);
+#define DBK_CASE(DD)                                                        \
+  case DD:                                                                  \
+    return launch_count_d<DD>(L, eps2, edges, pruned, screen, reverse, s,   \
+                              pairs);
     DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
     DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)
     DBK_CASE(64)

@@ -85,6 +85,11 @@ typedef enum dbscan_status {
                                         arithmetic); results are identical,
                                         far fewer distances are evaluated
                                         when d is small */
+#define DBSCAN_FLAG_REVERSE_SCHEDULE 0x10u /* for testing: walk the count
+                                             pass's work items, the recorded
+                                             pairs and the tile merge's
+                                             blocks in reverse order; the
+                                             results must not change */
 #define DBSCAN_FLAG_SCREEN 0x8u /* decide most pairs of the count pass with
                                    the hoisted-norm form |y|^2 - 2 x.y
                                    (Wang et al. Sec. IV-B2) evaluated with

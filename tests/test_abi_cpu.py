@@ -116,6 +116,7 @@ def test_graph_invalid_arguments_rejected_before_device_work():
     assert _graph_status(x, 8, 2, 0.1, cap=10) == bad        # NULL col_idx
     assert _graph_status(x, 8, 2, 0.1, flags=0x2) == bad      # not for graphs
     assert _graph_status(x, 8, 2, 0.1, flags=0x80) == bad
+    assert _graph_status(x, 8, 2, 0.1, flags=0x10) == bad      # fits only
 
 
 def _status(points, n, d, eps, m, labels=True):

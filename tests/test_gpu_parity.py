@@ -345,6 +345,29 @@ def test_screen_edge_cases(apd, orc, flags, mode):
             assert_same(lab, cnt, want_l, want_c, f"{name} m={m}")
 
 
+def test_schedule_shake(apd, orc):
+    """Walking the count pass's items, the recorded pairs and the tile
+    merge's blocks in reverse order (and with another edge capacity, which
+    changes which merge runs and the order pairs are recorded in) gives
+    the same labels: the union-find result does not depend on the order
+    of the links."""
+    cases = [(datagen.collinear_chain(20000, 0.5), 0.5, 2),
+             (datagen.integer_lattice(120, 2), 1.0, 5),
+             (datagen.gaussian_blobs(30000, 3, seed=9, n_blobs=30, sigma=0.01,
+                                     noise_frac=0.1), 0.012, 6)]
+    x2, e2, m2, _ = datagen.make_workload(2)
+    cases.append((x2, e2, m2))
+    for x, eps, m in cases:
+        want_l, want_c, _ = orc.fit(x, eps, m)
+        for base in (0, 2, 4, 8):
+            for fl in (base, base | 0x10):
+                lab, cnt, _ = gpu_fit(apd, x, eps, m, flags=fl)
+                assert_same(lab, cnt, want_l, want_c, f"n={x.shape} flags={fl}")
+        lab, cnt, info = gpu_fit(apd, x, eps, m, flags=0x10, max_edges=1000)
+        assert info["merge_mode"] == 2
+        assert_same(lab, cnt, want_l, want_c, f"n={x.shape} small edge area")
+
+
 def test_relabel_contiguous(apd, orc):
     import torch
     for t, (x, eps, m) in enumerate(pins.small_cases(seed=303, count=30)):
