@@ -29,6 +29,21 @@
 // 2^100 (where products could overflow) every row gets lo = -inf,
 // hi = +inf and zero coefficients: all pairs are then decided exactly.
 // Padding rows are NaN throughout and never match.
+//
+// When the count pass forms v on the matrix cores (v_mfma_f32_16x16x4_f32,
+// widths >= 16), the order of the additions inside an instruction, whether
+// the products are rounded on their own, the rounding mode and the
+// handling of subnormals are not specified.  The bound is then taken for
+// any order of the D additions, with every product and every sum rounded
+// off by up to 2u (any of the usual rounding modes): a product passes at
+// most D + 1 roundings, n_y at most D after its own.  So
+//   k = u + 2.01 g'_{D+1}, g'_m = 2 m u / (1 - 2 m u),
+// (the factor 2.01 covers |n_y| + sum |2 x_k y_k| <= (2+u)|y|^2 + |x|^2)
+// plus, for subnormals flushed anywhere, an absolute
+//   (2D + 2) 2^-126 (1 + 2 sqrt(Y)):
+// each product or partial sum loses at most 2^-126, and a flushed input
+// changes a product by at most 2^-126 times the other factor, itself at
+// most 2 sqrt(Y).
 #include <cmath>
 
 #include "device.h"
@@ -82,18 +97,20 @@ template <int D>
 __global__ __launch_bounds__(256) void k_screen_rows(
     const float* __restrict__ pts, int64_t n_pad, float eps2,
     float* __restrict__ srow, float* __restrict__ ncol,
-    const Status* __restrict__ st) {
+    const Status* __restrict__ st, int matrix) {
   constexpr int S = row_stride(D);
   constexpr int SR = screen_stride(D);
   const double u = 0x1p-24, t = 0x1p-149;
   const double gD = D * u / (1.0 - D * u);
   const double g2 = (D + 2) * u / (1.0 - (D + 2) * u);
-  const double kap = u + 2.01 * gD;
+  const double gM = 2.0 * (D + 1) * u / (1.0 - 2.0 * (D + 1) * u);
+  const double kap = u + 2.01 * (matrix ? gM : gD);
   const double e2 = (double)eps2;
   const double L = (e2 - (D + 2) * t) / (1.0 + g2);
   const double H = (e2 + (D + 2) * t) / (1.0 - g2);
   const double Y = __longlong_as_double((long long)st->ymax_bits);
   const bool unsafe = st->screen_unsafe != 0;
+  const double flush = matrix ? (2.0 * D + 2.0) * 0x1p-126 * (1.0 + 2.0 * sqrt(Y)) : 0.0;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
        i += (int64_t)gridDim.x * blockDim.x) {
     const float* p = pts + i * S;
@@ -114,7 +131,7 @@ __global__ __launch_bounds__(256) void k_screen_rows(
         out[D] = __builtin_inff();
         out[D + 1] = __builtin_inff();
       } else {
-        const double m = kap * (x2 + Y) + (D + 1) * t +
+        const double m = kap * (x2 + Y) + (D + 1) * t + flush +
                          1e-12 * (fabs(L) + fabs(H) + x2 + Y);
         out[D] = __double2float_rd(L - x2 - m);
         out[D + 1] = __double2float_ru(H - x2 + m);
@@ -133,7 +150,8 @@ hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
 #define DBK_CASE(DD)                                                       \
   case DD:                                                                 \
     k_screen_rows<DD><<<grid, 256, 0, s>>>(pts, L.n_pad, eps2, L.srow,     \
-                                           L.ncol, L.status);              \
+                                           L.ncol, L.status,               \
+                                           screen_on_matrix_cores(DD));    \
     break;
     DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
     DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)

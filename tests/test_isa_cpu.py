@@ -46,7 +46,7 @@ def _screened(name):
 
 
 def test_count_kernels_have_no_fused_or_packed_fp32(asm):
-    bodies = kernel_bodies(asm["count"], "k_count")
+    bodies = kernel_bodies(asm["count"], "7k_countI")
     # 12 widths x (edges or not) x (pruned or not) x (screened or not)
     assert len(bodies) == 96
     exact = {k: v for k, v in bodies.items() if not _screened(k)}
@@ -64,7 +64,7 @@ def test_screened_count_kernels(asm):
     """Screened kernels use fused multiply-adds for the screen value only;
     packed fp32 never appears, and the exact distance (separate subtract,
     multiply and add) is still there for the undecided pairs."""
-    bodies = {k: v for k, v in kernel_bodies(asm["count"], "k_count").items()
+    bodies = {k: v for k, v in kernel_bodies(asm["count"], "7k_countI").items()
               if _screened(k)}
     assert len(bodies) == 48
     other = re.compile(r"\b(v_pk_(fma|mul|add)_f32|v_fma_mix\w*|v_(mad|mac)_f32|"
@@ -72,6 +72,21 @@ def test_screened_count_kernels(asm):
     for name, body in bodies.items():
         assert not other.search(body), name
         assert SCREEN_ALLOWED.search(body), name
+        assert "v_sub_f32" in body and "v_mul_f32" in body, name
+
+
+def test_matrix_core_screen_kernels(asm):
+    """The matrix-core screen forms its values with fp32 MFMA only (no
+    packed or mixed-precision arithmetic), and keeps the exact distance's
+    separate subtract, multiply and add for the undecided pairs."""
+    bodies = kernel_bodies(asm["count"], "12k_count_mfmaI")
+    assert len(bodies) == 20   # widths 16, 24, 32, 48, 64 x edges x pruned
+    other = re.compile(r"\b(v_pk_(fma|mul|add)_f32|v_fma_mix\w*|v_(mad|mac)_f32|"
+                       r"v_mad_legacy_f32|v_fmac_legacy_f32|v_dot\w*|"
+                       r"v_mfma_f32_\w+_(bf16|f16|xf32|i8|fp8|bf8)\w*)\b")
+    for name, body in bodies.items():
+        assert "v_mfma_f32_16x16x4_f32" in body or "v_mfma_f32_16x16x4f32" in body, name
+        assert not other.search(body), name
         assert "v_sub_f32" in body and "v_mul_f32" in body, name
 
 

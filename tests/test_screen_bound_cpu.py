@@ -8,6 +8,11 @@ way the screen-table and count kernels define them (the fused multiply-add
 chain is evaluated exactly and rounded once per step); the exact decision
 is the direct fp32 distance of the rational model in pins.py.  Every pair
 the screen settles must agree with it.
+
+For the screen on the matrix cores (widths 16 and up), whose summation
+order, product rounding and rounding mode are not specified, the screen
+value is formed under several such models, each exactly, against the
+widened thresholds of that path.
 """
 import math
 from fractions import Fraction
@@ -50,15 +55,17 @@ def round_up32(v):
     return f
 
 
-def thresholds(x2, Y, eps2, D, kap_scale=1.0):
+def thresholds(x2, Y, eps2, D, kap_scale=1.0, matrix=False):
     u, t = 2.0 ** -24, 2.0 ** -149
     gD = D * u / (1 - D * u)
     g2 = (D + 2) * u / (1 - (D + 2) * u)
-    kap = (u + 2.01 * gD) * kap_scale
+    gM = 2 * (D + 1) * u / (1 - 2 * (D + 1) * u)
+    kap = (u + 2.01 * (gM if matrix else gD)) * kap_scale
+    flush = (2 * D + 2) * 2.0 ** -126 * (1 + 2 * math.sqrt(Y)) * kap_scale if matrix else 0.0
     e2 = float(eps2)
     L = (e2 - (D + 2) * t) / (1 + g2)
     H = (e2 + (D + 2) * t) / (1 - g2)
-    m = kap * (x2 + Y) + (D + 1) * t + 1e-12 * (abs(L) + abs(H) + x2 + Y)
+    m = kap * (x2 + Y) + (D + 1) * t + flush + 1e-12 * (abs(L) + abs(H) + x2 + Y)
     return round_down32(L - x2 - m), round_up32(H - x2 + m)
 
 
@@ -85,14 +92,64 @@ def near_radius_pairs(rng, d, scale, eps, count):
     return out
 
 
-def check_pairs(pairs, eps, D, kap_scale=1.0):
+def round32(q, mode):
+    """A rational rounded to binary32 (gradual underflow) to nearest ("rn"),
+    toward zero ("rz"), up ("ru") or down ("rd")."""
+    r = pins.rn32(q)
+    if mode == "rn" or r == q:
+        return r
+    if mode == "rz":
+        mode = "rd" if q > 0 else "ru"
+    f = np.float32(float(r))
+    if mode == "ru" and r < q:
+        return Fraction(float(np.nextafter(f, np.float32(np.inf))))
+    if mode == "rd" and r > q:
+        return Fraction(float(np.nextafter(f, np.float32(-np.inf))))
+    return r
+
+
+def matrix_screen_value(x, y, D, mode, fused, order):
+    """The screen value as a matrix unit might form it: n_y plus D/4
+    instructions, instruction t adding the products of dims q*D/4 + t,
+    q = 0..3 (one per lane group).  Products exact or rounded on their own;
+    the four additions of an instruction in order, reversed, as a tree, or
+    with one rounding; every rounding in `mode`."""
+    kq = D // 4
+    a = [Fraction(float(np.float32(-2.0) * v)) for v in x] + [Fraction(0)] * (D - len(x))
+    b = [Fraction(float(v)) for v in y] + [Fraction(0)] * (D - len(y))
+    prods = [ak * bk for ak, bk in zip(a, b)]
+    if not fused:
+        prods = [round32(p, mode) for p in prods]
+    acc = Fraction(float(np.float32(sq_norm64(y))))
+    for t in range(kq):
+        grp = [prods[qq * kq + t] for qq in range(4)]
+        if order == "seq":
+            for p in grp:
+                acc = round32(acc + p, mode)
+        elif order == "rev":
+            for p in reversed(grp):
+                acc = round32(acc + p, mode)
+        elif order == "tree":
+            s01 = round32(grp[0] + grp[1], mode)
+            s23 = round32(grp[2] + grp[3], mode)
+            acc = round32(acc + round32(s01 + s23, mode), mode)
+        else:   # "wide": the instruction's sum rounded once
+            acc = round32(acc + sum(grp), mode)
+    return acc
+
+
+def check_pairs(pairs, eps, D, kap_scale=1.0, model=None):
     eps2 = pins.eps2_of(eps)
     # the set's largest squared norm, as the first screen kernel finds it
     Y = max(max(sq_norm64(x), sq_norm64(y)) for x, y in pairs)
     settled = {"in": 0, "out": 0, "exact": 0, "wrong": 0}
     for x, y in pairs:
-        lo, hi = thresholds(sq_norm64(x), Y, eps2, D, kap_scale)
-        v = screen_value(x, y)
+        lo, hi = thresholds(sq_norm64(x), Y, eps2, D, kap_scale,
+                            matrix=model is not None)
+        if model is None:
+            v = screen_value(x, y)
+        else:
+            v = np.float32(float(matrix_screen_value(x, y, D, *model)))
         exact = pins.exact_d2_rounded(x, y) <= eps2
         if v <= lo:
             settled["in"] += 1
@@ -138,3 +195,33 @@ def test_threshold_rounding_is_outward():
         lo, hi = round_down32(v), round_up32(v)
         assert float(lo) <= v <= float(hi) or (math.isinf(float(hi)) and v > 0) \
             or (math.isinf(float(lo)) and v < 0)
+
+
+# The screen on the matrix cores (widths 16 and up): its thresholds are
+# widened for an unspecified summation order, rounding and product rounding.
+MATRIX_CASES = [(16, 3.0, 0.2), (20, 1.0, 0.3), (32, 1.0, 0.3), (48, 2.0, 0.5),
+                (64, 1.0, 0.35), (64, 30.0, 1.0)]
+MODELS = [("rn", True, "seq"), ("rn", False, "tree"), ("rz", False, "rev"),
+          ("ru", False, "seq"), ("rd", True, "wide"), ("rd", False, "tree")]
+
+
+@pytest.mark.parametrize("d,scale,eps", MATRIX_CASES)
+def test_matrix_screen_decisions_agree_with_the_exact_distance(d, scale, eps):
+    rng = np.random.default_rng(7000 + 1000 * d + int(scale))
+    pairs = near_radius_pairs(rng, d, scale, eps, 60)
+    for model in MODELS:
+        settled = check_pairs(pairs, eps, compiled_width(d), model=model)
+        assert settled["wrong"] == 0, (model, settled)
+        if scale <= 3.0:
+            assert settled["in"] > 1 and settled["out"] > 0, (model, settled)
+
+
+def test_matrix_bound_without_the_rounding_terms_is_caught():
+    wrong = 0
+    for d, scale, eps in MATRIX_CASES:
+        rng = np.random.default_rng(7000 + 1000 * d + int(scale))
+        pairs = near_radius_pairs(rng, d, scale, eps, 60)
+        for model in MODELS:
+            wrong += check_pairs(pairs, eps, compiled_width(d), kap_scale=0.0,
+                                 model=model)["wrong"]
+    assert wrong > 0
