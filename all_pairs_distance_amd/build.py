@@ -23,10 +23,10 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdbscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "k_count.hip", "k_prep.hip", "k_merge.hip",
-           "k_prune.hip", "k_relabel.hip", "k_graph.hip",
+SOURCES = ["api.hip", "k_count.hip", "k_count_mfma.hip", "k_prep.hip",
+           "k_merge.hip", "k_prune.hip", "k_relabel.hip", "k_graph.hip",
            "k_screen.hip"]
-HEADERS = ["internal.h", "device.h"]
+HEADERS = ["internal.h", "device.h", "count_common.h"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

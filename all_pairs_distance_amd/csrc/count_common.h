@@ -1,0 +1,79 @@
+// Helpers shared by the count kernels (k_count.hip, k_count_mfma.hip):
+// the tile enumeration, the edge sink and the wave's LDS edge stage.
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+
+namespace dbk {
+
+// Upper-triangle tile t (row-major over I <= J of nb x nb blocks) -> (I, J).
+__device__ __forceinline__ void tile_coords(int64_t t, int64_t nb, int64_t& I,
+                                            int64_t& J) {
+  const double b = 2.0 * (double)nb + 1.0;
+  int64_t i = (int64_t)((b - sqrt(b * b - 8.0 * (double)t)) * 0.5);
+  if (i < 0) i = 0;
+  if (i > nb - 1) i = nb - 1;
+  while (i > 0 && i * nb - i * (i - 1) / 2 > t) --i;
+  while (i + 1 < nb && (i + 1) * nb - (i + 1) * i / 2 <= t) ++i;
+  I = i;
+  J = i + (t - (i * nb - i * (i - 1) / 2));
+}
+
+struct EdgeSink {
+  uint2* edges;
+  unsigned long long cap;
+  unsigned long long* counter;
+};
+
+// Order this wave's LDS accesses around a hand-over between lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Copy the wave's staged edges to the edge area (one atomic per flush).
+// Slots past the capacity are dropped; the host sees the overflow because
+// the counter then exceeds the capacity.
+__device__ __forceinline__ void flush_edges(uint2* stage, unsigned fill,
+                                            const EdgeSink& sink) {
+  wave_lds_sync();
+  unsigned long long base = 0;
+  if (lane_id() == 0) base = atomicAdd(sink.counter, (unsigned long long)fill);
+  base = uniform_u64(base);
+  for (unsigned k = lane_id(); k < fill; k += 64) {
+    const unsigned long long dst = base + k;
+    if (dst < sink.cap) sink.edges[dst] = stage[k];
+  }
+  wave_lds_sync();
+}
+
+// Work items of a count launch: the upper triangle of nb x nb blocks of T
+// points, each tile cut into chunks of `rows` rows.  A whole block of T
+// rows per item loads each column block once per tile (a pruned launch
+// keeps only some tiles and splits them into items of up to kRowsPerItem
+// rows for parallelism); fewer rows, down to one wave's 64, while the full
+// triangle would give under 4096 items.
+struct CountPlan {
+  int64_t nb, items;
+  int rows, chunks_log2;
+  unsigned grid;
+};
+
+inline CountPlan plan_count(int64_t n_pad, int T, bool pruned) {
+  CountPlan c;
+  c.nb = n_pad / T;
+  const int64_t tiles = c.nb * (c.nb + 1) / 2;
+  c.rows = pruned && kRowsPerItem < T ? kRowsPerItem : T;
+  while (c.rows > 64 && tiles * (T / c.rows) < 4096) c.rows >>= 1;
+  const int chunks = T / c.rows;  // both powers of two
+  c.chunks_log2 = 0;
+  while ((1 << c.chunks_log2) < chunks) ++c.chunks_log2;
+  c.items = tiles * chunks;
+  const int64_t max_grid = pruned ? 16384 : kMaxGrid;
+  c.grid = (unsigned)(c.items < max_grid ? c.items : max_grid);
+  return c;
+}
+
+}  // namespace dbk

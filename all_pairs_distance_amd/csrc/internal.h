@@ -108,9 +108,13 @@ hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s);
 hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
                         bool screen, bool reverse, hipStream_t s,
                         int64_t* pairs);
-// The screened count pass runs on the matrix cores for these widths; its
-// thresholds are then widened for the matrix unit's arithmetic.
-bool screen_on_matrix_cores(int D);
+// The screened count pass runs on the matrix cores for these widths
+// (launch_count_mfma); its thresholds are then widened for the matrix
+// unit's arithmetic.
+constexpr bool screen_on_matrix_cores(int D) { return D >= 16; }
+hipError_t launch_count_mfma(const Layout& L, float eps2, bool edges,
+                             bool pruned, bool reverse, hipStream_t s,
+                             int64_t* pairs);
 hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
                          hipStream_t s);
 size_t prune_sort_bytes(int64_t n_pad);

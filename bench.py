@@ -70,6 +70,7 @@ def parse():
 COUNTER_PROFILE = os.path.join(ROOT, "profiles",
                                "k_count_blobs_walks3d_n1000000_counters.md")
 COUNT_SOURCES = ["all_pairs_distance_amd/csrc/k_count.hip",
+                 "all_pairs_distance_amd/csrc/count_common.h",
                  "all_pairs_distance_amd/csrc/device.h",
                  "all_pairs_distance_amd/csrc/internal.h"]
 

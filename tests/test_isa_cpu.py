@@ -35,6 +35,7 @@ def asm(tmp_path_factory):
     d = tmp_path_factory.mktemp("asm")
     return {
         "count": open(build.device_assembly(str(d / "c.s"), "k_count.hip")).read(),
+        "mfma": open(build.device_assembly(str(d / "f.s"), "k_count_mfma.hip")).read(),
         "merge": open(build.device_assembly(str(d / "m.s"), "k_merge.hip")).read(),
         "prune": open(build.device_assembly(str(d / "p.s"), "k_prune.hip")).read(),
     }
@@ -47,8 +48,9 @@ def _screened(name):
 
 def test_count_kernels_have_no_fused_or_packed_fp32(asm):
     bodies = kernel_bodies(asm["count"], "7k_countI")
-    # 12 widths x (edges or not) x (pruned or not) x (screened or not)
-    assert len(bodies) == 96
+    # 12 widths x (edges or not) x (pruned or not), exact; the 7 widths
+    # below 16 also screened (the wider ones screen on the matrix cores)
+    assert len(bodies) == 48 + 28
     exact = {k: v for k, v in bodies.items() if not _screened(k)}
     assert len(exact) == 48
     for name, body in exact.items():
@@ -66,7 +68,7 @@ def test_screened_count_kernels(asm):
     multiply and add) is still there for the undecided pairs."""
     bodies = {k: v for k, v in kernel_bodies(asm["count"], "7k_countI").items()
               if _screened(k)}
-    assert len(bodies) == 48
+    assert len(bodies) == 28
     other = re.compile(r"\b(v_pk_(fma|mul|add)_f32|v_fma_mix\w*|v_(mad|mac)_f32|"
                        r"v_mad_legacy_f32|v_fmac_legacy_f32|v_dot\w*)\b")
     for name, body in bodies.items():
@@ -79,7 +81,7 @@ def test_matrix_core_screen_kernels(asm):
     """The matrix-core screen forms its values with fp32 MFMA only (no
     packed or mixed-precision arithmetic), and keeps the exact distance's
     separate subtract, multiply and add for the undecided pairs."""
-    bodies = kernel_bodies(asm["count"], "12k_count_mfmaI")
+    bodies = kernel_bodies(asm["mfma"], "12k_count_mfmaI")
     assert len(bodies) == 20   # widths 16, 24, 32, 48, 64 x edges x pruned
     other = re.compile(r"\b(v_pk_(fma|mul|add)_f32|v_fma_mix\w*|v_(mad|mac)_f32|"
                        r"v_mad_legacy_f32|v_fmac_legacy_f32|v_dot\w*|"
