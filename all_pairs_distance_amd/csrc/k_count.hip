@@ -32,7 +32,7 @@ namespace dbk {
 // screen keeps one more value per column point (its norm) and its own
 // masks, so it is given more registers.
 constexpr int count_waves(int D, bool edges, bool screen) {
-  return screen ? (D <= 2 ? 4 : D <= 4 ? 5 : D <= 16 ? 6 : 1)
+  return screen ? (D <= 2 ? 4 : D <= 4 ? 5 : D <= 16 ? (edges ? 6 : 5) : 1)
                 : (D <= 2 ? 5 : D <= 16 ? 8 : 1);
 }
 
@@ -79,7 +79,8 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            const float* __restrict__ boxes64,
                                            const float* __restrict__ boxes_w,
                                            const float* __restrict__ srow,
-                                           const float* __restrict__ ncol) {
+                                           const float* __restrict__ ncol,
+                                           float* rows_lds) {
   constexpr int S = row_stride(D);
   constexpr int SR = screen_stride(D);
   const int lane = lane_id();
@@ -115,9 +116,28 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                        eps2))
       continue;
     int rowv = 0;  // lane l: count of row rb+l over these columns
+    if (SCREEN) {
+      // the 64 rows' records (-2x, lo, hi) go to the wave's LDS area with
+      // one coalesced load (lane l: row rb + l); each row is then read
+      // back by all lanes from one address (a broadcast)
+      const float4* rp = (const float4*)(srow + (row0 + rb + lane) * SR);
+      float4* wp = (float4*)(rows_lds + lane * SR);
+      wave_lds_sync();
+#pragma unroll
+      for (int k = 0; k < SR / 4; ++k) wp[k] = rp[k];
+      wave_lds_sync();
+    }
     // row addresses advance by a constant per row (the screen's exact path
     // recomputes its point address instead of carrying a second pointer)
-    const float* next = SCREEN ? srow + (row0 + rb) * SR : pts + (row0 + rb) * S;
+    const float* next = SCREEN ? rows_lds : pts + (row0 + rb) * S;
+    // screened: the next row's coefficients and upper threshold are read
+    // while the current row is evaluated (the area has a spare 65th row)
+    float a_next[SCREEN ? D : 1], hi_next = 0.f;
+    if (SCREEN) {
+#pragma unroll
+      for (int k = 0; k < D; ++k) a_next[k] = rows_lds[k];
+      hi_next = rows_lds[D + 1];
+    }
 #pragma unroll 2
     for (int l = 0; l < 64; ++l) {
       const int64_t row = row0 + rb + l;
@@ -127,14 +147,14 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
       float val[P];
       float lo = 0.f, thr = eps2;
       if (SCREEN) {
-        // wave-uniform address: read through the constant address space so
-        // the row lands in SGPRs via scalar loads
-        const const_float_ptr sp = (const_float_ptr)cur;
         float a[D];
 #pragma unroll
-        for (int k = 0; k < D; ++k) a[k] = sp[k];
-        lo = sp[D];
-        thr = sp[D + 1];
+        for (int k = 0; k < D; ++k) a[k] = a_next[k];
+        thr = hi_next;
+#pragma unroll
+        for (int k = 0; k < D; ++k) a_next[k] = next[k];
+        hi_next = next[D + 1];
+        lo = cur[D];
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           float v = ny[p];
@@ -244,9 +264,12 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     int reverse) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
+  constexpr int SR = screen_stride(D);
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
+  __shared__ __attribute__((aligned(16))) float rows_all[SCREEN ? 4 * 65 * SR : 1];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint2* stage = stage_all + (EDGES ? wave * kEdgeStage : 0);
+  float* rows_lds = rows_all + (SCREEN ? wave * 65 * SR : 0);
   unsigned fill = 0;
   const EdgeSink sink{edges, cap, counter};
   // pruned: walk the kept block pairs (written by the previous kernel);
@@ -277,11 +300,11 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     if (I == J)
       count_item<D, P, true, EDGES, PRUNED, SCREEN>(
           pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, srow, ncol);
+          boxes_w, srow, ncol, rows_lds);
     else
       count_item<D, P, false, EDGES, PRUNED, SCREEN>(
           pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, srow, ncol);
+          boxes_w, srow, ncol, rows_lds);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
