@@ -26,6 +26,10 @@ CFLAGS = ["-O3", "-std=c11", "-march=x86-64-v3", "-fopenmp",
 
 OK, BAD_ARG, NONFINITE, NO_MEMORY, FTZ_SET = 0, -1, -2, -4, -7
 
+# Which distance decides "within eps" (oracle.h): the direct fp32 sum of
+# squared differences, or the hoisted-norm form T + P - sum 2 x_k y_k.
+FORMS = {"direct": 0, "expanded": 1}
+
 
 class OracleError(RuntimeError):
     def __init__(self, status: int):
@@ -59,27 +63,41 @@ class Oracle:
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.oracle_d2.argtypes = [f32p, f32p, ctypes.c_int32]
         lib.oracle_d2.restype = ctypes.c_float
+        lib.oracle_sq_norm.argtypes = [f32p, ctypes.c_int32]
+        lib.oracle_sq_norm.restype = ctypes.c_float
+        lib.oracle_d2_expanded.argtypes = [f32p, f32p, ctypes.c_int32]
+        lib.oracle_d2_expanded.restype = ctypes.c_float
         lib.oracle_eps2.argtypes = [ctypes.c_float]
         lib.oracle_eps2.restype = ctypes.c_float
         lib.oracle_fit.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_float, ctypes.c_int32, i32p, i32p,
                                    ctypes.c_int32]
         lib.oracle_fit.restype = ctypes.c_int
+        lib.oracle_fit_form.argtypes = lib.oracle_fit.argtypes + [ctypes.c_int32]
+        lib.oracle_fit_form.restype = ctypes.c_int
         lib.oracle_row_counts.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_float, i64p, ctypes.c_int64,
                                           i32p, ctypes.c_int32]
         lib.oracle_row_counts.restype = ctypes.c_int
+        lib.oracle_row_counts_form.argtypes = (lib.oracle_row_counts.argtypes
+                                               + [ctypes.c_int32])
+        lib.oracle_row_counts_form.restype = ctypes.c_int
         lib.oracle_row_neighbours.argtypes = [f32p, ctypes.c_int64,
                                               ctypes.c_int32, ctypes.c_float,
                                               ctypes.c_int64, i64p,
                                               ctypes.c_int64]
         lib.oracle_row_neighbours.restype = ctypes.c_int64
+        lib.oracle_row_neighbours_form.argtypes = (
+            lib.oracle_row_neighbours.argtypes + [ctypes.c_int32])
+        lib.oracle_row_neighbours_form.restype = ctypes.c_int64
         lib.oracle_relabel.argtypes = [i32p, ctypes.c_int64, i32p, i32p]
         lib.oracle_relabel.restype = ctypes.c_int64
         lib.oracle_graph.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
                                      ctypes.c_float, i64p,
                                      ctypes.POINTER(i32p), ctypes.c_int32]
         lib.oracle_graph.restype = ctypes.c_int64
+        lib.oracle_graph_form.argtypes = lib.oracle_graph.argtypes + [ctypes.c_int32]
+        lib.oracle_graph_form.restype = ctypes.c_int64
         lib.oracle_free.argtypes = [ctypes.c_void_p]
         lib.oracle_free.restype = None
         lib.oracle_last_fit_seconds.argtypes = []
@@ -102,21 +120,36 @@ class Oracle:
         return np.float32(self.lib.oracle_d2(a.ctypes.data_as(f32p),
                                              b.ctypes.data_as(f32p), a.size))
 
+    def d2_expanded(self, a, b) -> np.float32:
+        """The hoisted-norm distance of two points (norms computed here)."""
+        a = np.ascontiguousarray(a, dtype=np.float32).ravel()
+        b = np.ascontiguousarray(b, dtype=np.float32).ravel()
+        assert a.shape == b.shape
+        f32p = ctypes.POINTER(ctypes.c_float)
+        return np.float32(self.lib.oracle_d2_expanded(
+            a.ctypes.data_as(f32p), b.ctypes.data_as(f32p), a.size))
+
+    def sq_norm(self, a) -> np.float32:
+        a = np.ascontiguousarray(a, dtype=np.float32).ravel()
+        return np.float32(self.lib.oracle_sq_norm(
+            a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), a.size))
+
     def eps2(self, eps) -> np.float32:
         return np.float32(self.lib.oracle_eps2(float(np.float32(eps))))
 
-    def fit(self, points, eps, min_pts, n_threads: int = 0):
+    def fit(self, points, eps, min_pts, n_threads: int = 0,
+            form: str = "direct"):
         """Returns (labels int32[N], counts int32[N], seconds)."""
         x = self._pts(points)
         n, d = x.shape
         labels = np.empty(n, dtype=np.int32)
         counts = np.empty(n, dtype=np.int32)
-        st = self.lib.oracle_fit(
+        st = self.lib.oracle_fit_form(
             x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n, d,
             float(np.float32(eps)), int(min_pts),
             labels.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
             counts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-            int(n_threads))
+            int(n_threads), FORMS[form])
         if st != OK:
             raise OracleError(st)
         return labels, counts, self.lib.oracle_last_fit_seconds()
@@ -147,18 +180,18 @@ class Oracle:
             raise OracleError(int(k))
         return out, sizes[:k].copy(), int(k)
 
-    def graph(self, points, eps, n_threads: int = 0):
+    def graph(self, points, eps, n_threads: int = 0, form: str = "direct"):
         """Sparse eps-graph: (row_ptr int64[n+1], col_idx int32[nnz])."""
         x = self._pts(points)
         n, d = x.shape
         row_ptr = np.zeros(n + 1, dtype=np.int64)
         i32p = ctypes.POINTER(ctypes.c_int32)
         col = i32p()
-        nnz = self.lib.oracle_graph(
+        nnz = self.lib.oracle_graph_form(
             x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n, d,
             float(np.float32(eps)),
             row_ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-            ctypes.byref(col), int(n_threads))
+            ctypes.byref(col), int(n_threads), FORMS[form])
         if nnz < 0:
             raise OracleError(int(nnz))
         try:
@@ -168,30 +201,33 @@ class Oracle:
             self.lib.oracle_free(col)
         return row_ptr, col_idx
 
-    def row_counts(self, points, eps, rows, n_threads: int = 0) -> np.ndarray:
+    def row_counts(self, points, eps, rows, n_threads: int = 0,
+                   form: str = "direct") -> np.ndarray:
         x = self._pts(points)
         n, d = x.shape
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         out = np.empty(rows.size, dtype=np.int32)
-        st = self.lib.oracle_row_counts(
+        st = self.lib.oracle_row_counts_form(
             x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n, d,
             float(np.float32(eps)),
             rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size,
-            out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_threads))
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(n_threads),
+            FORMS[form])
         if st != OK:
             raise OracleError(st)
         return out
 
-    def row_neighbours(self, points, eps, i) -> np.ndarray:
+    def row_neighbours(self, points, eps, i, form: str = "direct") -> np.ndarray:
         x = self._pts(points)
         n, d = x.shape
         cap = 1024
         while True:
             out = np.empty(cap, dtype=np.int64)
-            c = self.lib.oracle_row_neighbours(
+            c = self.lib.oracle_row_neighbours_form(
                 x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n, d,
                 float(np.float32(eps)), int(i),
-                out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), cap)
+                out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), cap,
+                FORMS[form])
             if c < 0:
                 raise OracleError(int(c))
             if c <= cap:

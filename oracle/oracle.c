@@ -57,6 +57,69 @@ float oracle_d2(const float* a, const float* b, int32_t d) {
   return s;
 }
 
+/* Squared norm in fp32: squares and their sum rounded, k ascending. */
+float oracle_sq_norm(const float* a, int32_t d) {
+  float s = a[0] * a[0];
+  for (int32_t k = 1; k < d; ++k) {
+    float q = a[k] * a[k];
+    s = s + q;
+  }
+  return s;
+}
+
+/* The hoisted-norm form of Wang et al. Sec. IV-B2: with T = |a|^2 and
+ * P = |b|^2 computed once per point, and the doubled coordinates 2 a_k
+ * (exact), dist = T + P - (2a_0 b_0 + 2a_1 b_1 + ...).  Every product and
+ * every sum is rounded on its own, the products summed in k order, then
+ * (T + P) and finally the subtraction. */
+float oracle_d2_expanded_from_norms(const float* a, const float* b, int32_t d,
+                                    float ta, float pb) {
+  float inner = (2.0f * a[0]) * b[0];
+  for (int32_t k = 1; k < d; ++k) {
+    float q = (2.0f * a[k]) * b[k];
+    inner = inner + q;
+  }
+  float s = ta + pb;
+  return s - inner;
+}
+
+float oracle_d2_expanded(const float* a, const float* b, int32_t d) {
+  return oracle_d2_expanded_from_norms(a, b, d, oracle_sq_norm(a, d),
+                                       oracle_sq_norm(b, d));
+}
+
+/* Neighbour test of points i and j under the chosen form; `norms` holds
+ * every point's oracle_sq_norm for the hoisted-norm form. */
+static int within(int32_t form, const float* p, int32_t d, const float* norms,
+                  int64_t i, int64_t j, float eps2) {
+  const float* a = p + i * (int64_t)d;
+  const float* b = p + j * (int64_t)d;
+  if (form == ORACLE_FORM_EXPANDED)
+    return oracle_d2_expanded_from_norms(a, b, d, norms[i], norms[j]) <= eps2;
+  return oracle_d2(a, b, d) <= eps2;
+}
+
+/* The per-point norms the hoisted-norm form needs (NULL otherwise, or on
+ * allocation failure with *oom set). */
+static float* form_norms(int32_t form, const float* p, int64_t n, int32_t d,
+                         int nt, int* oom) {
+  *oom = 0;
+  if (form != ORACLE_FORM_EXPANDED || n == 0) return NULL;
+  float* norms = (float*)malloc((size_t)n * sizeof(float));
+  if (!norms) {
+    *oom = 1;
+    return NULL;
+  }
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int64_t i = 0; i < n; ++i) norms[i] = oracle_sq_norm(p + i * (int64_t)d, d);
+  return norms;
+}
+
+static int check_form(int32_t form) {
+  return (form == ORACLE_FORM_DIRECT || form == ORACLE_FORM_EXPANDED) ? ORACLE_OK
+                                                                       : ORACLE_BAD_ARG;
+}
+
 static int check_args(const float* p, int64_t n, int32_t d, float eps,
                       int32_t min_pts) {
   if (n < 0 || n > (int64_t)INT32_MAX || d < 1 || min_pts < 1) return ORACLE_BAD_ARG;
@@ -113,7 +176,15 @@ static int edge_push(edge_buf* e, int32_t i, int32_t j) {
 int oracle_fit(const float* p, int64_t n, int32_t d, float eps,
                int32_t min_pts, int32_t* labels, int32_t* counts_out,
                int32_t n_threads) {
+  return oracle_fit_form(p, n, d, eps, min_pts, labels, counts_out, n_threads,
+                         ORACLE_FORM_DIRECT);
+}
+
+int oracle_fit_form(const float* p, int64_t n, int32_t d, float eps,
+                    int32_t min_pts, int32_t* labels, int32_t* counts_out,
+                    int32_t n_threads, int32_t form) {
   int st = check_args(p, n, d, eps, min_pts);
+  if (st == ORACLE_OK) st = check_form(form);
   if (st != ORACLE_OK) return st;
   if (n > 0 && labels == NULL) return ORACLE_BAD_ARG;
   if (host_flushes_denormals()) return ORACLE_FTZ_SET;
@@ -132,18 +203,19 @@ int oracle_fit(const float* p, int64_t n, int32_t d, float eps,
   int32_t* parent = (int32_t*)malloc((size_t)n * sizeof(int32_t));
   int32_t* bmin = (int32_t*)malloc((size_t)n * sizeof(int32_t));
   int32_t* first = (int32_t*)malloc((size_t)n * sizeof(int32_t));
-  if (!count || !core || !parent || !bmin || !first) {
-    free(count); free(core); free(parent); free(bmin); free(first);
+  int norms_oom = 0;
+  float* norms = form_norms(form, p, n, d, nt, &norms_oom);
+  if (!count || !core || !parent || !bmin || !first || norms_oom) {
+    free(count); free(core); free(parent); free(bmin); free(first); free(norms);
     return ORACLE_NO_MEMORY;
   }
 
   /* 1. neighbour count of every point, itself included. */
 #pragma omp parallel for schedule(dynamic, 64) num_threads(nt)
   for (int64_t i = 0; i < n; ++i) {
-    const float* pi = p + i * (int64_t)d;
     int64_t c = 0;
     for (int64_t j = 0; j < n; ++j)
-      if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) ++c;
+      if (within(form, p, d, norms, i, j, eps2)) ++c;
     count[i] = (int32_t)c;
   }
 
@@ -169,10 +241,9 @@ int oracle_fit(const float* p, int64_t n, int32_t d, float eps,
 #pragma omp for schedule(dynamic, 8)
       for (int64_t i = b0; i < b1; ++i) {
         if (!core[i]) continue;
-        const float* pi = p + i * (int64_t)d;
         for (int64_t j = i + 1; j < n; ++j) {
           if (!core[j]) continue;
-          if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2)
+          if (within(form, p, d, norms, i, j, eps2))
             if (edge_push(mine, (int32_t)i, (int32_t)j) != ORACLE_OK) {
 #pragma omp atomic write
               oom = 1;
@@ -188,7 +259,7 @@ int oracle_fit(const float* p, int64_t n, int32_t d, float eps,
     free(bufs);
   }
   if (oom) {
-    free(count); free(core); free(parent); free(bmin); free(first);
+    free(count); free(core); free(parent); free(bmin); free(first); free(norms);
     return ORACLE_NO_MEMORY;
   }
 
@@ -197,9 +268,8 @@ int oracle_fit(const float* p, int64_t n, int32_t d, float eps,
 #pragma omp parallel for schedule(dynamic, 64) num_threads(nt)
   for (int64_t i = 0; i < n; ++i) {
     if (core[i]) continue;
-    const float* pi = p + i * (int64_t)d;
     for (int64_t c = 0; c < n; ++c) {
-      if (core[c] && oracle_d2(pi, p + c * (int64_t)d, d) <= eps2) {
+      if (core[c] && within(form, p, d, norms, i, c, eps2)) {
         bmin[i] = (int32_t)c;
         break;
       }
@@ -219,14 +289,22 @@ int oracle_fit(const float* p, int64_t n, int32_t d, float eps,
 
   if (counts_out) memcpy(counts_out, count, (size_t)n * sizeof(int32_t));
   g_last_fit_seconds = now_seconds() - t0;
-  free(count); free(core); free(parent); free(bmin); free(first);
+  free(count); free(core); free(parent); free(bmin); free(first); free(norms);
   return ORACLE_OK;
 }
 
 int oracle_row_counts(const float* p, int64_t n, int32_t d, float eps,
                       const int64_t* rows, int64_t n_rows, int32_t* out,
                       int32_t n_threads) {
+  return oracle_row_counts_form(p, n, d, eps, rows, n_rows, out, n_threads,
+                                ORACLE_FORM_DIRECT);
+}
+
+int oracle_row_counts_form(const float* p, int64_t n, int32_t d, float eps,
+                           const int64_t* rows, int64_t n_rows, int32_t* out,
+                           int32_t n_threads, int32_t form) {
   int st = check_args(p, n, d, eps, 1);
+  if (st == ORACLE_OK) st = check_form(form);
   if (st != ORACLE_OK) return st;
   if (n_rows < 0 || (n_rows > 0 && (rows == NULL || out == NULL))) return ORACLE_BAD_ARG;
   if (host_flushes_denormals()) return ORACLE_FTZ_SET;
@@ -236,32 +314,46 @@ int oracle_row_counts(const float* p, int64_t n, int32_t d, float eps,
     if (rows[r] < 0 || rows[r] >= n) return ORACLE_BAD_ARG;
   const float eps2 = oracle_eps2(eps);
   const int nt = thread_count(n_threads);
+  int oom = 0;
+  float* norms = form_norms(form, p, n, d, nt, &oom);
+  if (oom) return ORACLE_NO_MEMORY;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
   for (int64_t r = 0; r < n_rows; ++r) {
-    const float* pi = p + rows[r] * (int64_t)d;
     int64_t c = 0;
     for (int64_t j = 0; j < n; ++j)
-      if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) ++c;
+      if (within(form, p, d, norms, rows[r], j, eps2)) ++c;
     out[r] = (int32_t)c;
   }
+  free(norms);
   return ORACLE_OK;
 }
 
 int64_t oracle_row_neighbours(const float* p, int64_t n, int32_t d, float eps,
                               int64_t i, int64_t* out, int64_t cap) {
+  return oracle_row_neighbours_form(p, n, d, eps, i, out, cap,
+                                    ORACLE_FORM_DIRECT);
+}
+
+int64_t oracle_row_neighbours_form(const float* p, int64_t n, int32_t d,
+                                   float eps, int64_t i, int64_t* out,
+                                   int64_t cap, int32_t form) {
   int st = check_args(p, n, d, eps, 1);
+  if (st == ORACLE_OK) st = check_form(form);
   if (st != ORACLE_OK) return st;
   if (i < 0 || i >= n || cap < 0 || (cap > 0 && out == NULL)) return ORACLE_BAD_ARG;
   if (host_flushes_denormals()) return ORACLE_FTZ_SET;
   const float eps2 = oracle_eps2(eps);
-  const float* pi = p + i * (int64_t)d;
+  int oom = 0;
+  float* norms = form_norms(form, p, n, d, 1, &oom);
+  if (oom) return ORACLE_NO_MEMORY;
   int64_t c = 0;
   for (int64_t j = 0; j < n; ++j) {
-    if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) {
+    if (within(form, p, d, norms, i, j, eps2)) {
       if (c < cap) out[c] = j;
       ++c;
     }
   }
+  free(norms);
   return c;
 }
 
@@ -298,7 +390,15 @@ int64_t oracle_relabel(const int32_t* labels, int64_t n, int32_t* out,
 int64_t oracle_graph(const float* p, int64_t n, int32_t d, float eps,
                      int64_t* row_ptr, int32_t** col_idx_out,
                      int32_t n_threads) {
+  return oracle_graph_form(p, n, d, eps, row_ptr, col_idx_out, n_threads,
+                           ORACLE_FORM_DIRECT);
+}
+
+int64_t oracle_graph_form(const float* p, int64_t n, int32_t d, float eps,
+                          int64_t* row_ptr, int32_t** col_idx_out,
+                          int32_t n_threads, int32_t form) {
   int st = check_args(p, n, d, eps, 1);
+  if (st == ORACLE_OK) st = check_form(form);
   if (st != ORACLE_OK) return st;
   if (row_ptr == NULL || col_idx_out == NULL) return ORACLE_BAD_ARG;
   *col_idx_out = NULL;
@@ -309,9 +409,11 @@ int64_t oracle_graph(const float* p, int64_t n, int32_t d, float eps,
   if (n == 0) return 0;
   const float eps2 = oracle_eps2(eps);
   const int nt = thread_count(n_threads);
+  int norms_oom = 0;
+  float* norms = form_norms(form, p, n, d, nt, &norms_oom);
   int32_t** rows = (int32_t**)calloc((size_t)n, sizeof(int32_t*));
   int64_t* len = (int64_t*)calloc((size_t)n, sizeof(int64_t));
-  int oom = (rows == NULL || len == NULL);
+  int oom = (rows == NULL || len == NULL || norms_oom);
   if (!oom) {
 #pragma omp parallel num_threads(nt)
     {
@@ -323,10 +425,9 @@ int64_t oracle_graph(const float* p, int64_t n, int32_t d, float eps,
 #pragma omp for schedule(dynamic, 64)
       for (int64_t i = 0; i < n; ++i) {
         if (tmp == NULL) continue;
-        const float* pi = p + i * (int64_t)d;
         int64_t c = 0;
         for (int64_t j = 0; j < n; ++j)
-          if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++] = (int32_t)j;
+          if (within(form, p, d, norms, i, j, eps2)) tmp[c++] = (int32_t)j;
         rows[i] = (int32_t*)malloc((size_t)c * sizeof(int32_t));
         if (rows[i] == NULL) {
 #pragma omp atomic write
@@ -351,6 +452,7 @@ int64_t oracle_graph(const float* p, int64_t n, int32_t d, float eps,
   for (int64_t i = 0; rows && i < n; ++i) free(rows[i]);
   free(rows);
   free(len);
+  free(norms);
   if (oom) {
     free(col);
     return ORACLE_NO_MEMORY;

@@ -45,8 +45,25 @@ enum {
   ORACLE_FTZ_SET = -7      /* host FPU flushes denormals: results would differ */
 };
 
+/* Which distance decides "within eps":
+ *   ORACLE_FORM_DIRECT    sum_k fl(fl(x_k - y_k)^2), k ascending (above);
+ *   ORACLE_FORM_EXPANDED  the hoisted-norm form of Wang et al. Sec. IV-B2,
+ *     dist = T + P - sum_k (2 x_k) y_k with T = |x|^2, P = |y|^2 (each a
+ *     sum of rounded squares, k ascending), the products summed in k
+ *     order, then T + P, then the subtraction, every step rounded.  It
+ *     rounds differently from the direct form (and can even be negative),
+ *     so near the radius its decisions may differ. */
+enum { ORACLE_FORM_DIRECT = 0, ORACLE_FORM_EXPANDED = 1 };
+
 /* fp32 squared distance, k ascending, each operation rounded. */
 float oracle_d2(const float* a, const float* b, int32_t d);
+
+/* fp32 squared norm (squares and sum rounded, k ascending) and the
+ * hoisted-norm distance (from given norms, or computing them). */
+float oracle_sq_norm(const float* a, int32_t d);
+float oracle_d2_expanded_from_norms(const float* a, const float* b, int32_t d,
+                                    float ta, float pb);
+float oracle_d2_expanded(const float* a, const float* b, int32_t d);
 
 /* fl32(eps * eps). */
 float oracle_eps2(float eps);
@@ -58,16 +75,28 @@ int oracle_fit(const float* points, int64_t n, int32_t d, float eps,
                int32_t min_pts, int32_t* labels, int32_t* counts,
                int32_t n_threads);
 
+/* The same fit with the neighbour test of the given form. */
+int oracle_fit_form(const float* points, int64_t n, int32_t d, float eps,
+                    int32_t min_pts, int32_t* labels, int32_t* counts,
+                    int32_t n_threads, int32_t form);
+
 /* Neighbour counts of the listed rows only (for sampled checks on large
  * sets): counts_out[r] = |N(rows[r])| over all n points. */
 int oracle_row_counts(const float* points, int64_t n, int32_t d, float eps,
                       const int64_t* rows, int64_t n_rows, int32_t* counts_out,
                       int32_t n_threads);
+int oracle_row_counts_form(const float* points, int64_t n, int32_t d,
+                           float eps, const int64_t* rows, int64_t n_rows,
+                           int32_t* counts_out, int32_t n_threads,
+                           int32_t form);
 
 /* Indices j (ascending) with d2(i, j) <= eps2, at most cap of them written;
  * returns the full neighbour count, or a negative status. */
 int64_t oracle_row_neighbours(const float* points, int64_t n, int32_t d,
                               float eps, int64_t i, int64_t* out, int64_t cap);
+int64_t oracle_row_neighbours_form(const float* points, int64_t n, int32_t d,
+                                   float eps, int64_t i, int64_t* out,
+                                   int64_t cap, int32_t form);
 
 /* Contiguous cluster ids: clusters are numbered 0..K-1 in ascending order
  * of their label (their smallest member); noise stays -1.  out: n int32.
@@ -84,6 +113,9 @@ int64_t oracle_relabel(const int32_t* labels, int64_t n, int32_t* out,
 int64_t oracle_graph(const float* points, int64_t n, int32_t d, float eps,
                      int64_t* row_ptr, int32_t** col_idx_out,
                      int32_t n_threads);
+int64_t oracle_graph_form(const float* points, int64_t n, int32_t d, float eps,
+                          int64_t* row_ptr, int32_t** col_idx_out,
+                          int32_t n_threads, int32_t form);
 void oracle_free(void* ptr);
 
 /* Wall time of the last oracle_fit on this thread, seconds (steady clock,

@@ -98,12 +98,14 @@ def neighbour_lists(x: np.ndarray, eps) -> list[np.ndarray]:
 
 # ----------------------------------------------------- classic DBSCAN (BFS)
 
-def bfs_dbscan(x: np.ndarray, eps, min_pts: int):
+def bfs_dbscan(x: np.ndarray, eps, min_pts: int, nb=None):
     """Ester et al.'s expansion: visit points in index order, grow a cluster
     from each unvisited core point by breadth-first search over
     neighbourhoods, expanding only through core points.  Returns
-    (cluster id per point or -1, core mask, neighbour lists)."""
-    nb = neighbour_lists(x, eps)
+    (cluster id per point or -1, core mask, neighbour lists).  The lists
+    are the direct form's unless given."""
+    if nb is None:
+        nb = neighbour_lists(x, eps)
     n = x.shape[0]
     core = np.array([len(v) >= min_pts for v in nb], dtype=bool)
     unvisited, noise = -2, -1
@@ -597,7 +599,158 @@ def check_graph(o):
     assert row_ptr.tolist() == [0] and col_idx.size == 0
 
 
+# ------------------------------------------ the hoisted-norm (expanded) form
+# Wang et al. Sec. IV-B2 move the squared norms out of the distance:
+# dist = T + P - (2 t_x p_x + 2 t_y p_y + ...), T = |t|^2, P = |p|^2.
+# Read as binary32 arithmetic in the order written: each norm is a sum of
+# rounded squares (k ascending), the products 2 t_k p_k are rounded and
+# summed in k order, then T + P, then the subtraction.
+
+def exact_sq_norm_rounded(a) -> Fraction:
+    s = None
+    for v in np.asarray(a, np.float32).ravel():
+        q = rn32(Fraction(float(v)) ** 2)
+        s = q if s is None else rn32(s + q)
+    return s
+
+
+def exact_expanded_rounded(a, b) -> np.float32:
+    """The hoisted-norm distance in exact rational arithmetic with a
+    rounding after every step."""
+    a = np.asarray(a, np.float32).ravel()
+    b = np.asarray(b, np.float32).ravel()
+    inner = None
+    for x, y in zip(a, b):
+        q = rn32(2 * Fraction(float(x)) * Fraction(float(y)))
+        inner = q if inner is None else rn32(inner + q)
+    s = rn32(exact_sq_norm_rounded(a) + exact_sq_norm_rounded(b))
+    return np.float32(float(rn32(s - inner)))
+
+
+def expanded_to_all(x: np.ndarray, i: int) -> np.ndarray:
+    """The hoisted-norm distance from point i to every point, numpy float32
+    step by step (elementwise operations only, dimensions ascending)."""
+    x = np.asarray(x, np.float32)
+    norms = x[:, 0] * x[:, 0]
+    inner = (np.float32(2.0) * x[i, 0]) * x[:, 0]
+    for k in range(1, x.shape[1]):
+        norms = norms + x[:, k] * x[:, k]
+        inner = inner + (np.float32(2.0) * x[i, k]) * x[:, k]
+    return (norms[i] + norms) - inner
+
+
+def expanded_lists(x: np.ndarray, eps) -> list[np.ndarray]:
+    e2 = eps2_of(eps)
+    return [np.nonzero(expanded_to_all(x, i) <= e2)[0] for i in range(x.shape[0])]
+
+
+def far_cases(seed, count):
+    """Small sets far from the origin (centres 100 to 3000, spread over
+    eight radii) with the radius near the rounding scale of the hoisted-norm
+    form there, so the two forms decide many pairs differently and the
+    border points and merges differ too."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for t in range(count):
+        n = int(rng.integers(30, 90))
+        d = int(rng.choice([1, 2, 2, 3]))
+        centre = float(rng.choice([100.0, 300.0, 1000.0, 3000.0]))
+        eps = float(rng.choice([0.1, 0.3, 1.0]))
+        x = (centre + rng.random((n, d)) * eps * 8).astype(np.float32)
+        out.append((x, eps, int(rng.integers(2, 7))))
+    return out
+
+
+def check_expanded_exact(o, seed=17):
+    """The oracle's hoisted-norm distance equals the rational model bit for
+    bit, is symmetric, and lies within its forward error bound of the true
+    squared distance: |E - R| <= (u + 2.01 g_d)(|a|^2 + |b|^2) + 3(d+1) 2^-149."""
+    rng = np.random.default_rng(seed)
+    pairs = boundary_pairs() + random_pairs(rng, 250)
+    for x, eps, _ in far_cases(seed, 4):
+        pairs += [(x[0], x[k]) for k in range(1, min(x.shape[0], 8))]
+    for a, b in pairs:
+        got = o.d2_expanded(a, b)
+        want = exact_expanded_rounded(a, b)
+        assert got.tobytes() == want.tobytes(), (a, b, got, want)
+        assert o.d2_expanded(b, a).tobytes() == got.tobytes()
+        d = a.size
+        g = Fraction(d) * U32 / (1 - Fraction(d) * U32)
+        mags = sum(Fraction(float(v)) ** 2 for v in np.concatenate([a, b]))
+        bound = (U32 + Fraction(201, 100) * g) * mags + 3 * (d + 1) * Fraction(2) ** -149
+        assert abs(Fraction(float(got)) - exact_d2_real(a, b)) <= bound, (a, b)
+        assert o.sq_norm(a).tobytes() == np.float32(float(exact_sq_norm_rounded(a))).tobytes()
+
+
+def check_expanded_closed_forms(o, seed=19):
+    """Where every step is exact the form is the true squared distance:
+    integer coordinates up to 64 in up to 8 dimensions (norms and products
+    below 2^24).  A point is at distance exactly 0 from itself at any scale
+    (the inner sum is twice the norm, step by step).  On integer sets with
+    an integer radius both forms give the same fit."""
+    rng = np.random.default_rng(seed)
+    for _ in range(300):
+        d = int(rng.integers(1, 9))
+        a = rng.integers(-64, 65, d).astype(np.float32)
+        b = rng.integers(-64, 65, d).astype(np.float32)
+        want = float(np.sum((a.astype(np.int64) - b.astype(np.int64)) ** 2))
+        assert float(o.d2_expanded(a, b)) == want, (a, b)
+    for scale in (1e-30, 1e-3, 1.0, 7.0, 1e3, 1e6, 1e15):
+        for _ in range(20):
+            d = int(rng.integers(1, 65))
+            a = (rng.standard_normal(d) * scale).astype(np.float32)
+            assert float(o.d2_expanded(a, a)) == 0.0, (scale, a)
+    for t in range(6):
+        n = int(rng.integers(5, 120))
+        d = int(rng.integers(1, 6))
+        x = rng.integers(-20, 21, (n, d)).astype(np.float32)
+        eps = float(rng.choice([0.0, 1.0, 2.0, 3.0, 5.0]))
+        m = int(rng.integers(1, 6))
+        le, ce, _ = o.fit(x, eps, m, form="expanded")
+        ld, cd, _ = o.fit(x, eps, m)
+        assert np.array_equal(ce, cd) and np.array_equal(le, ld), (n, d, eps, m)
+
+
+def check_expanded_bfs(o, seed=61, count=30):
+    """The fit under the hoisted-norm form == breadth-first DBSCAN over the
+    neighbour lists of that form (numpy float32 step emulation), with the
+    canonical border and label rules; on random small sets and on sets far
+    from the origin where the two forms disagree."""
+    disagree = 0
+    for x, eps, m in small_cases(seed, count) + far_cases(seed, 24):
+        nb = expanded_lists(x, eps)
+        lab, core, _ = bfs_dbscan(x, eps, m, nb=nb)
+        want_lab = canonical_from_partition(lab, core, nb)
+        want_cnt = np.array([len(v) for v in nb], dtype=np.int32)
+        got_lab, got_cnt, _ = o.fit(x, eps, m, form="expanded")
+        assert np.array_equal(got_cnt, want_cnt), (x.shape, eps, m)
+        assert np.array_equal(got_lab, want_lab), (x.shape, eps, m)
+        _, direct_cnt, _ = o.fit(x, eps, m)
+        disagree += int(np.sum(direct_cnt != got_cnt))
+    assert disagree > 0   # the sample does hold pairs the forms decide apart
+
+
+def check_expanded_graph(o, seed=67):
+    """Graph rows, sampled row counts and row neighbour lists under the
+    hoisted-norm form equal that form's neighbour lists."""
+    for x, eps, m in far_cases(seed, 6) + small_cases(seed, 8):
+        nb = expanded_lists(x, eps)
+        row_ptr, col_idx = o.graph(x, eps, form="expanded")
+        check_graph_structure(x, eps, row_ptr, col_idx)
+        want_ptr = np.concatenate([[0], np.cumsum([len(v) for v in nb])])
+        assert np.array_equal(row_ptr, want_ptr), (x.shape, eps)
+        assert np.array_equal(col_idx, np.concatenate(nb).astype(np.int32))
+        rows = np.arange(0, x.shape[0], 3)
+        assert np.array_equal(o.row_counts(x, eps, rows, form="expanded"),
+                              np.array([len(nb[r]) for r in rows], np.int32))
+        for r in rows[:4]:
+            assert np.array_equal(o.row_neighbours(x, eps, int(r), form="expanded"),
+                                  nb[r].astype(np.int64))
+
+
 ALL_CHECKS = [check_handworked, check_d2_exact, check_d2_order_and_rounding,
               check_eps2, check_bfs, check_invariants, check_sklearn,
               check_kdtree_counts, check_components, check_closed_forms,
-              check_argument_errors, check_relabel, check_graph]
+              check_argument_errors, check_relabel, check_graph,
+              check_expanded_exact, check_expanded_closed_forms,
+              check_expanded_bfs, check_expanded_graph]

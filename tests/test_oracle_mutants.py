@@ -17,15 +17,16 @@ import pins
 ORACLE_DIR = os.path.dirname(oracle.__file__)
 
 COUNT_LOOP = ("    for (int64_t j = 0; j < n; ++j)\n"
-              "      if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) ++c;\n"
+              "      if (within(form, p, d, norms, i, j, eps2)) ++c;\n"
               "    count[i] = (int32_t)c;")
+GRAPH_TEST = "if (within(form, p, d, norms, i, j, eps2)) tmp[c++] = (int32_t)j;"
 
 MUTANTS = {
     # comparison at the radius made strict
     "strict_radius": [("<= eps2", "< eps2")],
     # a point no longer counts itself
     "self_excluded": [(COUNT_LOOP, COUNT_LOOP.replace(
-        "if (oracle_d2", "if (j != i && oracle_d2"))],
+        "if (within", "if (j != i && within"))],
     # core test made strict
     "core_strict": [("count[i] >= min_pts", "count[i] > min_pts")],
     # radius not squared
@@ -39,7 +40,7 @@ MUTANTS = {
     "reversed_sum": [("for (int32_t k = 0; k < d; ++k) {",
                       "for (int32_t k = d - 1; k >= 0; --k) {")],
     # row stride forgotten (transposed operand indexing)
-    "bad_stride": [(COUNT_LOOP, COUNT_LOOP.replace("p + j * (int64_t)d", "p + j"))],
+    "bad_stride": [("const float* b = p + j * (int64_t)d;", "const float* b = p + j;")],
     # clusters merged through non-core points
     "merge_through_border": [("          if (!core[j]) continue;\n", "")],
     # border point takes its highest-index core neighbour
@@ -54,16 +55,43 @@ MUTANTS = {
     "relabel_noise_zero": [("out[i] = l < 0 ? -1 : id[l];",
                             "out[i] = l < 0 ? 0 : id[l];")],
     # graph rows leave out the point itself
-    "graph_no_self": [("if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++] = (int32_t)j;",
-                       "if (j != i && oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++] = (int32_t)j;")],
+    "graph_no_self": [(GRAPH_TEST, GRAPH_TEST.replace("if (within", "if (j != i && within"))],
     # graph rows scanned in descending order
-    "graph_descending": [("        for (int64_t j = 0; j < n; ++j)\n          if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++]",
-                          "        for (int64_t j = n - 1; j >= 0; --j)\n          if (oracle_d2(pi, p + j * (int64_t)d, d) <= eps2) tmp[c++]")],
+    "graph_descending": [("        for (int64_t j = 0; j < n; ++j)\n          " + GRAPH_TEST,
+                          "        for (int64_t j = n - 1; j >= 0; --j)\n          " + GRAPH_TEST)],
     # graph radius made strict (only in the graph)
-    "graph_strict": [("<= eps2) tmp[c++]", "< eps2) tmp[c++]")],
+    "graph_strict": [(GRAPH_TEST, "if (within(form, p, d, norms, i, j, eps2) && "
+                                  "oracle_d2(p + i * (int64_t)d, p + j * (int64_t)d, d) != eps2) "
+                                  "tmp[c++] = (int32_t)j;")],
     # graph offsets shifted by one row
     "graph_offsets": [("row_ptr[i + 1] = row_ptr[i] + len[i];",
                        "row_ptr[i + 1] = row_ptr[i] + (i + 1 < n ? len[i + 1] : len[0]);")],
+    # hoisted-norm form: the goal point's coordinates not doubled
+    "expanded_not_doubled": [("float inner = (2.0f * a[0]) * b[0];", "float inner = a[0] * b[0];"),
+                             ("float q = (2.0f * a[k]) * b[k];", "float q = a[k] * b[k];")],
+    # hoisted-norm form: the inner sum added instead of subtracted
+    "expanded_plus": [("return s - inner;", "return s + inner;")],
+    # hoisted-norm form: one norm used twice
+    "expanded_one_norm": [("float s = ta + pb;", "float s = ta + ta;")],
+    # hoisted-norm form: inner products summed in descending dimension order
+    "expanded_inner_reversed": [(
+        "float inner = (2.0f * a[0]) * b[0];\n  for (int32_t k = 1; k < d; ++k) {",
+        "float inner = (2.0f * a[d - 1]) * b[d - 1];\n  for (int32_t k = d - 2; k >= 0; --k) {")],
+    # hoisted-norm form: (T - inner) + P instead of (T + P) - inner
+    "expanded_regrouped": [("float s = ta + pb;\n  return s - inner;",
+                            "float s = ta - inner;\n  return s + pb;")],
+    # hoisted-norm form: norms summed from the last dimension
+    "expanded_norm_reversed": [(
+        "float s = a[0] * a[0];\n  for (int32_t k = 1; k < d; ++k) {\n    float q = a[k] * a[k];",
+        "float s = a[d - 1] * a[d - 1];\n  for (int32_t k = d - 2; k >= 0; --k) {\n    float q = a[k] * a[k];")],
+    # the border step always uses the direct form
+    "expanded_border_direct": [("if (core[c] && within(form, p, d, norms, i, c, eps2)) {",
+                                "if (core[c] && within(ORACLE_FORM_DIRECT, p, d, norms, i, c, eps2)) {")],
+    # the graph always uses the direct form
+    "expanded_graph_direct": [(GRAPH_TEST, GRAPH_TEST.replace("within(form,", "within(ORACLE_FORM_DIRECT,"))],
+    # the form ignored in the merge of core pairs
+    "expanded_merge_direct": [("          if (within(form, p, d, norms, i, j, eps2))\n            if (edge_push",
+                               "          if (within(ORACLE_FORM_DIRECT, p, d, norms, i, j, eps2))\n            if (edge_push")],
     # border points treated as noise
     "no_borders": [("else if (bmin[i] >= 0) r = uf_find(parent, bmin[i]);",
                     "else if (0) r = 0;")],
