@@ -27,6 +27,7 @@ FLAG_FORCE_TILE_MERGE = 0x2
 FLAG_PRUNE_TILES = 0x4
 FLAG_SCREEN = 0x8
 FLAG_REVERSE_SCHEDULE = 0x10
+FLAG_EXPANDED = 0x20
 MAX_D = 64
 
 

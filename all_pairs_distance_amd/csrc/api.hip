@@ -34,7 +34,7 @@ static int64_t tile_capacity(int64_t n_pad, int D) {
   return all < kTileListCap ? all : kTileListCap;
 }
 
-constexpr int kRegions = 23;
+constexpr int kRegions = 24;
 
 // Region sizes in carve order; every region starts 256-byte aligned.
 static size_t regions(int64_t n_pad, int D, size_t* out) {
@@ -64,6 +64,7 @@ static size_t regions(int64_t n_pad, int D, size_t* out) {
       np / (64 * (size_t)lane_points(D)) * 2 * S * sizeof(float),  // boxes_w
       np * (size_t)screen_stride(D) * sizeof(float),  // srow
       np * sizeof(float),            // ncol
+      np * sizeof(float),            // nexp
       sort_bytes(n_pad),             // radix sort scratch (last)
   };
   size_t total = 0;
@@ -108,8 +109,9 @@ bool carve(Layout& L, void* ws, size_t ws_bytes) {
   L.boxes_w = reinterpret_cast<float*>(b + off[19]);
   L.srow = reinterpret_cast<float*>(b + off[20]);
   L.ncol = reinterpret_cast<float*>(b + off[21]);
-  L.sort_tmp = b + off[22];
-  L.sort_tmp_bytes = need - off[22];
+  L.nexp = reinterpret_cast<float*>(b + off[22]);
+  L.sort_tmp = b + off[23];
+  L.sort_tmp_bytes = need - off[23];
   L.bytes_min = need;
   const size_t spare = ws_bytes - need;
   L.edges = reinterpret_cast<uint2*>(b + need);
@@ -128,7 +130,8 @@ constexpr uint32_t kKnownFlags = DBSCAN_FLAG_TIME_PHASES |
                                   DBSCAN_FLAG_FORCE_TILE_MERGE |
                                   DBSCAN_FLAG_PRUNE_TILES |
                                   DBSCAN_FLAG_SCREEN |
-                                  DBSCAN_FLAG_REVERSE_SCHEDULE;
+                                  DBSCAN_FLAG_REVERSE_SCHEDULE |
+                                  DBSCAN_FLAG_EXPANDED;
 
 int check_args(int64_t n, int32_t d, float eps, int32_t min_pts) {
   if (n < 0 || n > (int64_t)INT32_MAX) return DBSCAN_ERR_INVALID_ARG;
@@ -270,6 +273,8 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   int st = check_args(n, d, eps, min_pts);
   if (st != DBSCAN_OK) return st;
   if (flags & ~kKnownFlags) return DBSCAN_ERR_INVALID_ARG;
+  if ((flags & DBSCAN_FLAG_EXPANDED) && (flags & DBSCAN_FLAG_PRUNE_TILES))
+    return DBSCAN_ERR_INVALID_ARG;
   if (n > 0 && (d_points == nullptr || d_labels == nullptr))
     return DBSCAN_ERR_INVALID_ARG;
   if (n == 0) return DBSCAN_OK;
@@ -283,6 +288,7 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   L.D = pick_dim(d);
   L.stride = row_stride(L.D);
   L.n_pad = pad_points(n);
+  L.expanded = (flags & DBSCAN_FLAG_EXPANDED) != 0;
   if (!carve(L, d_workspace, workspace_bytes)) return DBSCAN_ERR_WORKSPACE;
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -292,7 +298,8 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   const bool want_edges =
       L.edge_cap > 0 && !(flags & DBSCAN_FLAG_FORCE_TILE_MERGE);
   const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
-  const bool screen = (flags & DBSCAN_FLAG_SCREEN) != 0;
+  // the hoisted-norm form is always evaluated behind the screen
+  const bool screen = (flags & (DBSCAN_FLAG_SCREEN | DBSCAN_FLAG_EXPANDED)) != 0;
   const bool reverse = (flags & DBSCAN_FLAG_REVERSE_SCHEDULE) != 0;
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
   int64_t pass1 = 0, pass2 = 0;
@@ -451,7 +458,9 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   int st = check_args(n, d, eps, 1);
   if (st != DBSCAN_OK) return st;
   if (flags & ~(DBSCAN_FLAG_TIME_PHASES | DBSCAN_FLAG_PRUNE_TILES |
-                DBSCAN_FLAG_SCREEN))
+                DBSCAN_FLAG_SCREEN | DBSCAN_FLAG_EXPANDED))
+    return DBSCAN_ERR_INVALID_ARG;
+  if ((flags & DBSCAN_FLAG_EXPANDED) && (flags & DBSCAN_FLAG_PRUNE_TILES))
     return DBSCAN_ERR_INVALID_ARG;
   if (d_row_ptr == nullptr || col_capacity < 0 ||
       (col_capacity > 0 && d_col_idx == nullptr) ||
@@ -477,6 +486,7 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   L.D = pick_dim(d);
   L.stride = row_stride(L.D);
   L.n_pad = pad_points(n);
+  L.expanded = (flags & DBSCAN_FLAG_EXPANDED) != 0;
   if (!carve_graph(L, G, d_workspace, workspace_bytes))
     return DBSCAN_ERR_WORKSPACE;
   const size_t sort_need = graph_sort_bytes(n);
@@ -485,7 +495,7 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   volatile float eps_v = eps;
   const float eps2 = eps_v * eps_v;
   const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
-  const bool screen = (flags & DBSCAN_FLAG_SCREEN) != 0;
+  const bool screen = (flags & (DBSCAN_FLAG_SCREEN | DBSCAN_FLAG_EXPANDED)) != 0;
   const unsigned long long col_cap = (unsigned long long)col_capacity;
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
   int64_t pass1 = 0;

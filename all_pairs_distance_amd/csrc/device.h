@@ -25,6 +25,24 @@ __device__ __forceinline__ float dist2(const float* a, const float* b) {
   return s;
 }
 
+// The hoisted-norm form of Wang et al. Sec. IV-B2 as a fixed binary32
+// evaluation: with ta = |a|^2 and pb = |b|^2 given (rounded squares summed
+// in k order), the products (2 a_k) b_k (doubling is exact) rounded and
+// summed in k order, then ta + pb, then the subtraction.  Padding dims are
+// zero on both sides; their +-0 products leave the result unchanged.
+template <int D>
+__device__ __forceinline__ float expanded_d2(const float* a, const float* b,
+                                             float ta, float pb) {
+  float inner = (2.f * a[0]) * b[0];
+#pragma unroll
+  for (int k = 1; k < D; ++k) {
+    const float q = (2.f * a[k]) * b[k];
+    inner = inner + q;
+  }
+  const float s = ta + pb;
+  return s - inner;
+}
+
 // Read-only global memory seen through the constant address space: loads
 // from wave-uniform addresses through such a pointer become scalar loads.
 typedef const float __attribute__((address_space(4)))* const_float_ptr;

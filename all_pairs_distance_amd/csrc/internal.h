@@ -59,6 +59,9 @@ constexpr int64_t kTileListCap = (int64_t)1 << 24;
 struct Layout {
   int64_t n, n_pad;
   int d, D, stride;
+  // neighbours decided with the hoisted-norm form T + P - sum 2 x_k y_k
+  // (always screened, never pruned) instead of the direct distance
+  bool expanded;
   // carved from the workspace
   Status* status;
   float* pts;          // [n_pad][stride], padded rows are NaN
@@ -84,6 +87,8 @@ struct Layout {
   unsigned long long tile_cap;
   float* srow;         // [n_pad][screen_stride] screen row table
   float* ncol;         // [n_pad] fp32 squared norm of each point (screen)
+  float* nexp;         // [n_pad] squared norm as the hoisted-norm form
+                       //         takes it: rounded squares summed in k order
   void* sort_tmp;      // radix sort scratch
   size_t sort_tmp_bytes;
   uint2* edges;        // edge area (may be empty)

@@ -80,6 +80,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            const float* __restrict__ boxes_w,
                                            const float* __restrict__ srow,
                                            const float* __restrict__ ncol,
+                                           const float* __restrict__ nexp,
                                            float* rows_lds) {
   constexpr int S = row_stride(D);
   constexpr int SR = screen_stride(D);
@@ -190,14 +191,23 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
           }
           if (amb) {
             // some pair of this row lies inside the bound: decide the
-            // row's pairs with the exact distance
+            // row's pairs with the exact distance (or, given its norms,
+            // the exact hoisted-norm form)
             const const_float_ptr rp = (const_float_ptr)(pts + row * S);
             float xr[D];
 #pragma unroll
             for (int k = 0; k < D; ++k) xr[k] = rp[k];
+            if (!PRUNED && nexp != nullptr) {
+              const float tr = ((const_float_ptr)nexp)[row];
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-              m[p] = ballot(dist2<D>(xr, xc[p]) <= eps2);
+              for (int p = 0; p < P; ++p)
+                m[p] = ballot(expanded_d2<D>(xr, xc[p], tr,
+                                             nexp[colw + p * 64 + lane]) <= eps2);
+            } else {
+#pragma unroll
+              for (int p = 0; p < P; ++p)
+                m[p] = ballot(dist2<D>(xr, xc[p]) <= eps2);
+            }
           }
         } else {
 #pragma unroll
@@ -261,7 +271,7 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     unsigned long long tile_cap, const int* __restrict__ perm,
     const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
     const float* __restrict__ srow, const float* __restrict__ ncol,
-    int reverse) {
+    const float* __restrict__ nexp, int reverse) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int SR = screen_stride(D);
@@ -300,11 +310,11 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     if (I == J)
       count_item<D, P, true, EDGES, PRUNED, SCREEN>(
           pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, srow, ncol, rows_lds);
+          boxes_w, srow, ncol, nexp, rows_lds);
     else
       count_item<D, P, false, EDGES, PRUNED, SCREEN>(
           pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, srow, ncol, rows_lds);
+          boxes_w, srow, ncol, nexp, rows_lds);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
@@ -320,7 +330,8 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   pts, c.nb, c.chunks_log2, c.rows, c.items, eps2, L.count,                 \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
-      L.boxes_w, L.srow, L.ncol, reverse ? 1 : 0
+      L.boxes_w, L.srow, L.ncol, screen && L.expanded ? L.nexp : nullptr,   \
+      reverse ? 1 : 0
 #define DBK_LAUNCH(E, PR, SC) \
   k_count<D, E, PR, SC><<<c.grid, kThreads, 0, s>>>(DBK_COUNT_ARGS)
   if (screen) {

@@ -66,6 +66,25 @@ __device__ __forceinline__ bool wave_exact_within(const float* __restrict__ xp,
   return d2 <= eps2;
 }
 
+// The hoisted-norm form of one pair, by the whole wave: lane k forms the
+// rounded product (2 x_k) y_k, the products are added in ascending k from
+// the lanes in turn, then (tx + ty) minus that sum.  Same value in every
+// lane.
+template <int D>
+__device__ __forceinline__ bool wave_expanded_within(
+    const float* __restrict__ xp, const float* __restrict__ yp, float tx,
+    float ty, float eps2) {
+  const int k = lane_id();
+  float pr = 0.f;
+  if (k < D) pr = (2.f * xp[k]) * yp[k];
+  float inner = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), 0));
+#pragma unroll
+  for (int kk = 1; kk < D; ++kk)
+    inner = inner + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), kk));
+  const float s = tx + ty;
+  return s - inner <= eps2;
+}
+
 // waves per SIMD the register budget is held to (the widths listed fit
 // three without spilling)
 constexpr int mfma_waves(int D, bool edges) {
@@ -82,7 +101,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
     unsigned long long tile_cap, const int* __restrict__ perm,
     const float* __restrict__ srow, const float* __restrict__ ncol,
-    int reverse) {
+    const float* __restrict__ nexp, int reverse) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
@@ -209,16 +228,28 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
         for (unsigned w = amb; w != 0; w &= w - 1) {
           const int b = __builtin_ctz(w);
           const int g = b >> 2, r = b & 3;
-          const float* xp = pts + (rbase + 4 * q + r) * S;
-          const float* yp = pts + (colw + g * 16 + l16) * S;
-          float t0 = xp[0] - yp[0];
-          float d2 = t0 * t0;
-          for (int k = 1; k < D; ++k) {
-            const float t = xp[k] - yp[k];
-            const float q2 = t * t;
-            d2 = d2 + q2;
+          const int64_t i = rbase + 4 * q + r, j = colw + g * 16 + l16;
+          const float* xp = pts + i * S;
+          const float* yp = pts + j * S;
+          float v;
+          if (!PRUNED && nexp != nullptr) {
+            float inner = (2.f * xp[0]) * yp[0];
+            for (int k = 1; k < D; ++k) {
+              const float pr = (2.f * xp[k]) * yp[k];
+              inner = inner + pr;
+            }
+            const float s = nexp[i] + nexp[j];
+            v = s - inner;
+          } else {
+            float t0 = xp[0] - yp[0];
+            v = t0 * t0;
+            for (int k = 1; k < D; ++k) {
+              const float t = xp[k] - yp[k];
+              const float q2 = t * t;
+              v = v + q2;
+            }
           }
-          if (d2 <= eps2) flag |= 1u << b;
+          if (v <= eps2) flag |= 1u << b;
         }
       } else {
         // a few: one pair at a time across the wave
@@ -228,7 +259,12 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
           const int b = __builtin_ctz(bits);
           const int64_t i = rbase + 4 * (src >> 4) + (b & 3);
           const int64_t j = colw + (b >> 2) * 16 + (src & 15);
-          const bool in = wave_exact_within<D>(pts + i * S, pts + j * S, eps2);
+          const bool in =
+              (!PRUNED && nexp != nullptr)
+                  ? wave_expanded_within<D>(pts + i * S, pts + j * S,
+                                            ((const_float_ptr)nexp)[i],
+                                            ((const_float_ptr)nexp)[j], eps2)
+                  : wave_exact_within<D>(pts + i * S, pts + j * S, eps2);
           if (lane == src) {
             if (in) flag |= 1u << b;
             amb &= amb - 1;
@@ -337,7 +373,7 @@ static hipError_t launch_count_mfma_d(const Layout& L, float eps2, bool edges,
   pts, c.nb, c.chunks_log2, c.rows, c.items, eps2, L.count,                  \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                  \
       &L.status->n_edges, L.tiles, &L.status->n_tiles, L.tile_cap, L.perm,   \
-      L.srow, L.ncol, reverse ? 1 : 0
+      L.srow, L.ncol, L.expanded ? L.nexp : nullptr, reverse ? 1 : 0
   if (edges && pruned)
     k_count_mfma<D, true, true><<<c.grid, kThreads, 0, s>>>(DBK_MFMA_ARGS);
   else if (edges)

@@ -60,12 +60,15 @@ hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
 
 typedef const unsigned char __attribute__((address_space(4)))* const_u8_ptr;
 
-template <int D>
+// EXPANDED: pairs are decided with the hoisted-norm form, from the norm
+// table nexp (indexed by original point).
+template <int D, bool EXPANDED>
 __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     const float* __restrict__ pts, const float* __restrict__ core_pts,
     const int* __restrict__ core_list, const unsigned char* __restrict__ core,
     int64_t row_blocks, int64_t col_blocks, float eps2, int* parent,
-    int* __restrict__ bmin, int reverse) {
+    int* __restrict__ bmin, const float* __restrict__ nexp, int64_t n_core,
+    int reverse) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
@@ -80,12 +83,16 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     const int64_t colw = cblk * T + (int64_t)wave * 64 * P;
     float xc[P][D];
     int cidx[P];
+    float pc[EXPANDED ? P : 1];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int64_t c = colw + p * 64 + lane;
       cidx[p] = core_list[c];
 #pragma unroll
       for (int k = 0; k < D; ++k) xc[p][k] = core_pts[c * S + k];
+      // columns past the cores have NaN coordinates and never match (their
+      // core_list entries are not written): no norm is read for them
+      if (EXPANDED) pc[p] = c < n_core ? nexp[cidx[p]] : 0.f;
     }
     for (int rb = 0; rb < kRowsPerItem; rb += 64) {
       int rowmin = INT_MAX;  // lane l: lowest core neighbour of row rb+l
@@ -96,10 +103,12 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
 #pragma unroll
         for (int k = 0; k < D; ++k) xr[k] = rp[k];
         const bool row_core = ((const_u8_ptr)core)[row] != 0;
+        const float tr = EXPANDED ? ((const_float_ptr)nexp)[row] : 0.f;
         int best = INT_MAX;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          const bool nb = dist2<D>(xr, xc[p]) <= eps2;
+          const bool nb = (EXPANDED ? expanded_d2<D>(xr, xc[p], tr, pc[p])
+                                    : dist2<D>(xr, xc[p])) <= eps2;
           const uint64_t m = ballot(nb);
           if (m) {
             if (row_core) {
@@ -128,10 +137,14 @@ static hipError_t launch_merge_tiles_d(const Layout& L, float eps2,
   if (row_blocks == 0 || col_blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)(col_blocks < 4096 ? col_blocks : 4096),
                   (unsigned)(row_blocks < 4096 ? row_blocks : 4096));
-  k_merge_tiles<D><<<grid, kThreads, 0, s>>>(L.pts, L.core_pts, L.core_list,
-                                             L.core, row_blocks, col_blocks,
-                                             eps2, L.parent, L.bmin,
-                                             reverse ? 1 : 0);
+  if (L.expanded)
+    k_merge_tiles<D, true><<<grid, kThreads, 0, s>>>(
+        L.pts, L.core_pts, L.core_list, L.core, row_blocks, col_blocks, eps2,
+        L.parent, L.bmin, L.nexp, n_core, reverse ? 1 : 0);
+  else
+    k_merge_tiles<D, false><<<grid, kThreads, 0, s>>>(
+        L.pts, L.core_pts, L.core_list, L.core, row_blocks, col_blocks, eps2,
+        L.parent, L.bmin, nullptr, n_core, reverse ? 1 : 0);
   if (pairs) *pairs = L.n_pad * nc_pad;
   return hipGetLastError();
 }

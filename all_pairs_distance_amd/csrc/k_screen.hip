@@ -30,6 +30,18 @@
 // hi = +inf and zero coefficients: all pairs are then decided exactly.
 // Padding rows are NaN throughout and never match.
 //
+// With the hoisted-norm form as the decision (DBSCAN_FLAG_EXPANDED), the
+// exact value is E = fl(fl(T + P) - I): T, P the fp32 norms (rounded
+// squares summed in k order), I the k-ordered sum of the rounded products
+// (2 x_k) y_k.  Each of T, P and I passes at most D roundings and T + P one
+// more, so with z = fl(T + P) - I,
+//   |z - R| <= (u + 2.01 g_D)(|x|^2 + |y|^2) + 3(D+1) t,
+// and, rounding being monotone, z <= eps2 gives E <= eps2 while
+// z > eps2 (1 + 2u) + 2t gives E > eps2.  The thresholds then bracket
+// those two conditions instead of L and H:
+//   lo = RD(eps2 - |x|^2 - m'),  hi = RU(eps2 (1 + 2u) + 2t - |x|^2 + m'),
+//   m' = m + (u + 2.01 g_D)(|x|^2 + Y) + 3(D+1) t.
+//
 // When the count pass forms v on the matrix cores (v_mfma_f32_16x16x4_f32,
 // widths >= 16), the order of the additions inside an instruction, whether
 // the products are rounded on their own, the rounding mode and the
@@ -66,10 +78,23 @@ __device__ __forceinline__ double sq_norm64(const float* __restrict__ p, int S) 
   return s;
 }
 
-// Pass 1: fp32 norms of every point and the largest fp64 squared norm.
+// The squared norm as the hoisted-norm form takes it: rounded squares
+// summed in k order in fp32 (padding dims are zero and add nothing).
+__device__ __forceinline__ float sq_norm32(const float* __restrict__ p, int S) {
+  float s = p[0] * p[0];
+  for (int k = 1; k < S; ++k) {
+    const float q = p[k] * p[k];
+    s = s + q;
+  }
+  return s;
+}
+
+// Pass 1: fp32 norms of every point and the largest fp64 squared norm
+// (and, for the hoisted-norm form, its own fp32 norm of every point).
 __global__ __launch_bounds__(256) void k_screen_norms(
     const float* __restrict__ pts, int64_t n_pad, int S,
-    float* __restrict__ ncol, Status* __restrict__ st) {
+    float* __restrict__ ncol, float* __restrict__ nexp,
+    Status* __restrict__ st) {
   double ymax = 0.0;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -80,6 +105,7 @@ __global__ __launch_bounds__(256) void k_screen_norms(
     } else {
       ncol[i] = __builtin_nanf("");
     }
+    if (nexp) nexp[i] = sq_norm32(pts + i * S, S);
   }
   for (int off = 32; off > 0; off >>= 1) {
     const double o = __shfl_xor(ymax, off);
@@ -97,7 +123,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_screen_rows(
     const float* __restrict__ pts, int64_t n_pad, float eps2,
     float* __restrict__ srow, float* __restrict__ ncol,
-    const Status* __restrict__ st, int matrix) {
+    const Status* __restrict__ st, int matrix, int expanded) {
   constexpr int S = row_stride(D);
   constexpr int SR = screen_stride(D);
   const double u = 0x1p-24, t = 0x1p-149;
@@ -105,6 +131,8 @@ __global__ __launch_bounds__(256) void k_screen_rows(
   const double g2 = (D + 2) * u / (1.0 - (D + 2) * u);
   const double gM = 2.0 * (D + 1) * u / (1.0 - 2.0 * (D + 1) * u);
   const double kap = u + 2.01 * (matrix ? gM : gD);
+  // the hoisted-norm form's own error against R (see above)
+  const double kapE = expanded ? u + 2.01 * gD : 0.0;
   const double e2 = (double)eps2;
   const double L = (e2 - (D + 2) * t) / (1.0 + g2);
   const double H = (e2 + (D + 2) * t) / (1.0 - g2);
@@ -131,10 +159,18 @@ __global__ __launch_bounds__(256) void k_screen_rows(
         out[D] = __builtin_inff();
         out[D + 1] = __builtin_inff();
       } else {
-        const double m = kap * (x2 + Y) + (D + 1) * t + flush +
-                         1e-12 * (fabs(L) + fabs(H) + x2 + Y);
-        out[D] = __double2float_rd(L - x2 - m);
-        out[D + 1] = __double2float_ru(H - x2 + m);
+        if (expanded) {
+          const double hiE = e2 * (1.0 + 2.0 * u) + 2.0 * t;
+          const double m = (kap + kapE) * (x2 + Y) + 4.0 * (D + 1) * t +
+                           flush + 1e-12 * (e2 + x2 + Y);
+          out[D] = __double2float_rd(e2 - x2 - m);
+          out[D + 1] = __double2float_ru(hiE - x2 + m);
+        } else {
+          const double m = kap * (x2 + Y) + (D + 1) * t + flush +
+                           1e-12 * (fabs(L) + fabs(H) + x2 + Y);
+          out[D] = __double2float_rd(L - x2 - m);
+          out[D + 1] = __double2float_ru(H - x2 + m);
+        }
       }
     }
     for (int k = D + 2; k < SR; ++k) out[k] = 0.f;
@@ -144,14 +180,16 @@ __global__ __launch_bounds__(256) void k_screen_rows(
 hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
                          hipStream_t s) {
   k_screen_norms<<<grid_for_s(L.n_pad, 256 * 4), 256, 0, s>>>(
-      pts, L.n_pad, L.stride, L.ncol, L.status);
+      pts, L.n_pad, L.stride, L.ncol, L.expanded ? L.nexp : nullptr,
+      L.status);
   const unsigned grid = grid_for_s(L.n_pad, 256 * 4);
   switch (L.D) {
 #define DBK_CASE(DD)                                                       \
   case DD:                                                                 \
     k_screen_rows<DD><<<grid, 256, 0, s>>>(pts, L.n_pad, eps2, L.srow,     \
                                            L.ncol, L.status,               \
-                                           screen_on_matrix_cores(DD));    \
+                                           screen_on_matrix_cores(DD),     \
+                                           L.expanded ? 1 : 0);            \
     break;
     DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
     DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)

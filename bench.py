@@ -302,13 +302,16 @@ def main():
     }
     out["config"]["tiles_kept"] = last.tiles_kept
     out["config"]["tiles_total"] = last.tiles_total
-    def mode_leg(fl, what):
+    def mode_leg(fl, what, ref=None):
+        # ref: the oracle digests this mode must reproduce (the fit's own
+        # unless the mode changes the distance form)
+        ref = g if ref is None else ref
         m_infos, m_ms, _ = timed(fl, args.steps, 1)
         m_last = m_infos[-1]
         m_parity = "unchecked"
-        if not args.no_parity and parity != "unchecked":
-            ok = (digest(labels.cpu().numpy()) == g["labels_sha256"]
-                  and digest(counts.cpu().numpy()) == g["counts_sha256"])
+        if not args.no_parity and parity != "unchecked" and ref:
+            ok = (digest(labels.cpu().numpy()) == ref["labels_sha256"]
+                  and digest(counts.cpu().numpy()) == ref["counts_sha256"])
             m_parity = "labels+counts bit-exact vs oracle" if ok else "MISMATCH vs oracle"
         return {
             "what": what,
@@ -337,6 +340,12 @@ def main():
         out["pruned_screen_mode"] = mode_leg(
             flags | apd.FLAG_SCREEN | apd.FLAG_PRUNE_TILES,
             "tile pruning and the screened count pass together")
+        out["expanded_mode"] = mode_leg(
+            (flags & ~apd.FLAG_PRUNE_TILES) | apd.FLAG_EXPANDED,
+            "fit deciding pairs with the hoisted-norm form T + P - sum "
+            "2 x_k y_k itself (DBSCAN_FLAG_EXPANDED; screened); checked "
+            "against the oracle's same form",
+            ref=(g or {}).get("expanded") or {})
     if not args.no_graph_line:
         out["graph_mode"] = graph_leg(apd, torch, xt, n, d, eps, stream,
                                       args.steps, g, args.no_parity)

@@ -101,6 +101,25 @@ typedef enum dbscan_status {
                                    results are identical to the exact pass
                                    and about d instead of 3d operations are
                                    spent per pair */
+#define DBSCAN_FLAG_EXPANDED 0x20u /* decide "within eps" with the
+                                      hoisted-norm distance of Wang et al.
+                                      Sec. IV-B2 itself instead of the
+                                      direct one: dist = T + P - sum_k
+                                      (2 x_k) y_k, T = |x|^2 and P = |y|^2
+                                      each summed from rounded squares in
+                                      k order, the products summed in k
+                                      order, then T + P, then the
+                                      subtraction, every step a binary32
+                                      operation.  It rounds differently
+                                      (the error grows with the norms, and
+                                      the value can be negative), so
+                                      results near the radius may differ
+                                      from the default form.  Implies
+                                      DBSCAN_FLAG_SCREEN (the screen then
+                                      brackets this form); not combined
+                                      with DBSCAN_FLAG_PRUNE_TILES, whose
+                                      bound is for the direct form
+                                      (DBSCAN_ERR_INVALID_ARG) */
 
 /* What a fit did; filled by dbscan_fit_device_ex when info != NULL. */
 typedef struct dbscan_info {
@@ -211,8 +230,8 @@ int dbscan_relabel_device(const int32_t* d_labels, int64_t n, int32_t* d_ids,
  *   d_workspace, workspace_bytes  caller-owned device scratch, 256-byte
  *              aligned, at least dbscan_graph_workspace_bytes(n, d, pairs)
  *              for the number of neighbour pairs i<j, (nnz - n) / 2.
- *   flags      DBSCAN_FLAG_PRUNE_TILES, DBSCAN_FLAG_SCREEN and
- *              DBSCAN_FLAG_TIME_PHASES; for
+ *   flags      DBSCAN_FLAG_PRUNE_TILES, DBSCAN_FLAG_SCREEN,
+ *              DBSCAN_FLAG_EXPANDED and DBSCAN_FLAG_TIME_PHASES; for
  *              this call ms_core times the row offsets, ms_merge the
  *              scatter of the pairs and ms_label the row sort.
  *   info       optional; n_edges = neighbour pairs i<j, edge_capacity =

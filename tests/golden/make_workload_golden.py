@@ -3,8 +3,10 @@ synthetic workloads, as SHA-256 digests and summary counts.
 
 Only the oracle is called (never the GPU library).  Run from the repository
 root:  python tests/golden/make_workload_golden.py [--threads T] [--graph]
-[keys...]   (--graph adds the digest of the sparse eps-graph to existing
-entries, leaving the fit's fields as they are)
+[--expanded] [keys...]   (--graph adds the digest of the sparse eps-graph
+to existing entries, leaving the fit's fields as they are; --expanded adds,
+under "expanded", the fit and graph digests of the hoisted-norm distance
+form)
 Each workload is written as soon as it finishes, so a partial run keeps its
 finished entries.  The GPU parity tests compare the library's labels and
 neighbour counts with these digests bit for bit, after checking that the
@@ -62,6 +64,7 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--threads", type=int, default=0)
     ap.add_argument("--graph", action="store_true")
+    ap.add_argument("--expanded", action="store_true")
     ap.add_argument("keys", nargs="*", type=int, default=[1, 2, 3, 4, 5])
     args = ap.parse_args()
     table = {}
@@ -73,6 +76,30 @@ def main() -> None:
         x, eps, min_pts, w = datagen.make_workload(k)
         print(f"workload {k} {w.name}: n={w.n} d={w.d}", flush=True)
         t0 = time.time()
+        if args.expanded:
+            entry = table[str(k)]
+            assert entry["points_sha256"] == datagen.sha256_points(x)
+            labels, counts, fit_s = o.fit(x, eps, min_pts, n_threads=args.threads,
+                                          form="expanded")
+            sub = {
+                "labels_sha256": digest(labels.astype("<i4")),
+                "counts_sha256": digest(counts.astype("<i4")),
+                **summary(labels, counts, min_pts),
+                "oracle_fit_seconds": round(fit_s, 3),
+            }
+            del labels, counts
+            if k <= 3:   # the graphs of the two largest sets take too long
+                row_ptr, col_idx = o.graph(x, eps, n_threads=args.threads,
+                                           form="expanded")
+                sub["graph_sha256"] = graph_digest(row_ptr, col_idx)
+                sub["graph_nnz"] = int(row_ptr[-1])
+                del row_ptr, col_idx
+            entry["expanded"] = sub
+            with open(OUT, "w") as f:
+                json.dump(table, f, indent=1, sort_keys=True)
+                f.write("\n")
+            print(k, json.dumps(sub), f"wall {time.time() - t0:.1f}s", flush=True)
+            continue
         if args.graph:
             entry = table[str(k)]
             assert entry["points_sha256"] == datagen.sha256_points(x)

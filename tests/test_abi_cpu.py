@@ -117,6 +117,7 @@ def test_graph_invalid_arguments_rejected_before_device_work():
     assert _graph_status(x, 8, 2, 0.1, flags=0x2) == bad      # not for graphs
     assert _graph_status(x, 8, 2, 0.1, flags=0x80) == bad
     assert _graph_status(x, 8, 2, 0.1, flags=0x10) == bad      # fits only
+    assert _graph_status(x, 8, 2, 0.1, flags=0x24) == bad      # expanded + pruned
 
 
 def _status(points, n, d, eps, m, labels=True):
@@ -142,6 +143,11 @@ def test_invalid_arguments_rejected_before_device_work():
     st = apd.dbscan_fit_device_ex(x.ctypes.data, 8, 2, 0.1, 1, ws.ctypes.data,
                                   None, ws.ctypes.data, 16, None, 0x80, None)
     assert st == _capi.ERR_INVALID_ARG               # unknown flag bit
+    st = apd.dbscan_fit_device_ex(x.ctypes.data, 8, 2, 0.1, 1, ws.ctypes.data,
+                                  None, ws.ctypes.data, 16, None,
+                                  _capi.FLAG_EXPANDED | _capi.FLAG_PRUNE_TILES,
+                                  None)
+    assert st == _capi.ERR_INVALID_ARG   # the pruning bound is for the direct form
 
 
 def _gpu_visible():
