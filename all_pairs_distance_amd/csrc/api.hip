@@ -52,7 +52,7 @@ static size_t regions(int64_t n_pad, int D, size_t* out) {
       np * sizeof(int),              // core_list
       np * S * sizeof(float),        // core_pts
       (np / 1024 + 1) * sizeof(unsigned),  // block_sums
-      6 * sizeof(unsigned),          // bbox
+      12 * sizeof(unsigned),         // bbox
       np * sizeof(unsigned),         // keys_in
       np * sizeof(unsigned),         // keys_out
       np * sizeof(int),              // idx_in

@@ -74,7 +74,7 @@ struct Layout {
   float* core_pts;     // [n_pad][stride] their coordinates (tile merge)
   unsigned* block_sums;// [n_pad / 1024 + 1] compaction scan
   // tile pruning (used only when asked for)
-  unsigned* bbox;      // [6] order-encoded min/max of 3 coordinates
+  unsigned* bbox;      // [12] order-encoded min/max of up to 6 key coordinates
   unsigned* keys_in;   // [n_pad] sort keys
   unsigned* keys_out;  // [n_pad]
   int* idx_in;         // [n_pad] 0..n_pad-1

@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--max-edges", type=int, default=1 << 30)
     ap.add_argument("--tile-merge", action="store_true",
                     help="force the second tile pass instead of the edge list")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle sample run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
