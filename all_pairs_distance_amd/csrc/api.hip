@@ -34,7 +34,7 @@ static int64_t tile_capacity(int64_t n_pad, int D) {
   return all < kTileListCap ? all : kTileListCap;
 }
 
-constexpr int kRegions = 24;
+constexpr int kRegions = 25;
 
 // Region sizes in carve order; every region starts 256-byte aligned.
 static size_t regions(int64_t n_pad, int D, size_t* out) {
@@ -65,6 +65,7 @@ static size_t regions(int64_t n_pad, int D, size_t* out) {
       np * (size_t)screen_stride(D) * sizeof(float),  // srow
       np * sizeof(float),            // ncol
       np * sizeof(float),            // nexp
+      (7 * S + 1) * sizeof(float),   // pca
       sort_bytes(n_pad),             // radix sort scratch (last)
   };
   size_t total = 0;
@@ -110,8 +111,9 @@ bool carve(Layout& L, void* ws, size_t ws_bytes) {
   L.srow = reinterpret_cast<float*>(b + off[20]);
   L.ncol = reinterpret_cast<float*>(b + off[21]);
   L.nexp = reinterpret_cast<float*>(b + off[22]);
-  L.sort_tmp = b + off[23];
-  L.sort_tmp_bytes = need - off[23];
+  L.pca = reinterpret_cast<float*>(b + off[23]);
+  L.sort_tmp = b + off[24];
+  L.sort_tmp_bytes = need - off[24];
   L.bytes_min = need;
   const size_t spare = ws_bytes - need;
   L.edges = reinterpret_cast<uint2*>(b + need);

@@ -83,6 +83,7 @@ struct Layout {
   float* boxes;        // [nb][2][stride] block bounding boxes
   float* boxes64;      // [n_pad/64][2][stride] boxes of 64-point row groups
   float* boxes_w;      // [n_pad/(64P)][2][stride] boxes of a wave's columns
+  float* pca;          // [7*stride + 1] sort-key directions of wide points
   uint2* tiles;        // kept block pairs
   unsigned long long tile_cap;
   float* srow;         // [n_pad][screen_stride] screen row table

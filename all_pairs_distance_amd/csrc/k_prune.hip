@@ -1,8 +1,8 @@
 // Exact tile pruning for the neighbour-count pass (an opt-in mode).
 //
 // The points are put in a locality-preserving order (a Morton key over the
-// first min(d,3) coordinates, or the first 6 for points of 16 or more
-// dimensions, sorted), each block of T consecutive sorted
+// first min(d,3) coordinates, or, for points of 16 or more dimensions, over
+// six principal directions, sorted), each block of T consecutive sorted
 // points gets its bounding box, and a block pair (I, J) is skipped when the
 // boxes are provably farther apart than eps in the same fp32 arithmetic the
 // distance uses:
@@ -46,9 +46,156 @@ __device__ __forceinline__ float ord_f(unsigned u) {
 // Most coordinates a sort key covers.
 constexpr int kKeyDims = 6;
 
+// ---- sort key of wide points: principal directions --------------------
+// For points of 16 or more dimensions the key covers the coordinates along
+// the six leading principal directions of a strided sample of the points,
+// plus one bit that sets apart points far off those directions (squared
+// residual above the sample's mean): on embedded blobs with uniform noise
+// the noise then sorts apart from the blobs and the blobs' blocks stay
+// compact.  Only the order depends on it; the box bound decides.
+constexpr int kPcaSample = 1024;
+constexpr int kPcaIters = 30;
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// One workgroup of 256 threads.  out: the sample mean [S], then kKeyDims
+// orthonormal directions [S each], then the sample's mean squared residual
+// off them.
+__global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
+                                             int64_t n, int S, int d,
+                                             float* __restrict__ out) {
+  __shared__ float tile[64][65];
+  __shared__ float mean[64];
+  __shared__ float cov[64][65];
+  __shared__ float vs[kKeyDims][64];
+  const int tid = threadIdx.x;
+  const int64_t m = n < kPcaSample ? n : kPcaSample;
+  const int64_t step = n / m;
+  // sample mean
+  float msum = 0.f;
+  for (int64_t s0 = 0; s0 < m; s0 += 64) {
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e >> 6, k = e & 63;
+      const int64_t smp = s0 + r;
+      tile[r][k] = (smp < m && k < d) ? pts[smp * step * S + k] : 0.f;
+    }
+    __syncthreads();
+    if (tid < 64)
+      for (int r = 0; r < 64; ++r) msum += tile[r][tid];
+    __syncthreads();
+  }
+  if (tid < 64) mean[tid] = msum / (float)m;
+  __syncthreads();
+  // scatter matrix of the centred sample; each thread a 4 x 4 block
+  const int k0 = 4 * (tid >> 4), l0 = 4 * (tid & 15);
+  float c[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) c[i][j] = 0.f;
+  for (int64_t s0 = 0; s0 < m; s0 += 64) {
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e >> 6, k = e & 63;
+      const int64_t smp = s0 + r;
+      tile[r][k] = (smp < m && k < d) ? pts[smp * step * S + k] - mean[k] : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < 64; ++r) {
+      float a[4], b[4];
+      for (int i = 0; i < 4; ++i) {
+        a[i] = tile[r][k0 + i];
+        b[i] = tile[r][l0 + i];
+      }
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) c[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) cov[k0 + i][l0 + j] = c[i][j];
+  __syncthreads();
+  // subspace iteration in wave 0: lane k holds component k of every
+  // direction; V <- orth(C V), modified Gram-Schmidt
+  if (tid < 64) {
+    const int k = tid;
+    float v[kKeyDims];
+    for (int j = 0; j < kKeyDims; ++j)   // a fixed full-rank start
+      v[j] = (k == j ? 4.f : 0.f) + (float)((k * (2 * j + 3) + j) % 7) - 3.f;
+    for (int it = 0; it < kPcaIters; ++it) {
+      for (int j = 0; j < kKeyDims; ++j) vs[j][k] = v[j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float w[kKeyDims];
+      for (int j = 0; j < kKeyDims; ++j) {
+        float acc = 0.f;
+        for (int l = 0; l < 64; ++l) acc += cov[k][l] * vs[j][l];
+        w[j] = acc;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int j = 0; j < kKeyDims; ++j) {
+        for (int i = 0; i < j; ++i) {
+          const float dot = wave_sum_f(w[j] * v[i]);
+          w[j] -= dot * v[i];
+        }
+        const float nrm = sqrtf(wave_sum_f(w[j] * w[j]));
+        v[j] = nrm > 0.f ? w[j] / nrm : 0.f;
+      }
+    }
+    // mean squared residual = (trace C - sum_j v_j' C v_j) / m
+    float cv[kKeyDims];
+    for (int j = 0; j < kKeyDims; ++j) vs[j][k] = v[j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float captured = 0.f;
+    for (int j = 0; j < kKeyDims; ++j) {
+      float acc = 0.f;
+      for (int l = 0; l < 64; ++l) acc += cov[k][l] * vs[j][l];
+      cv[j] = acc;
+      captured += v[j] * cv[j];
+    }
+    captured = wave_sum_f(captured);
+    const float trace = wave_sum_f(cov[k][k]);
+    if (k < S) {
+      out[k] = mean[k];
+      for (int j = 0; j < kKeyDims; ++j) out[(1 + j) * S + k] = k < d ? v[j] : 0.f;
+    }
+    if (k == 0) out[(1 + kKeyDims) * S] = (trace - captured) / (float)m;
+  }
+}
+
+// The KD key coordinates of point p: its first KD coordinates, or (with a
+// principal-direction table) its coordinates along those directions and
+// its squared residual off them.
+__device__ __forceinline__ void key_coords(const float* __restrict__ p, int KD,
+                                           int d, int S,
+                                           const float* __restrict__ pca,
+                                           float* y, float* r2) {
+  if (pca == nullptr) {
+    for (int k = 0; k < KD; ++k) y[k] = p[k];
+    *r2 = 0.f;
+    return;
+  }
+  float tot = 0.f;
+  for (int j = 0; j < kKeyDims; ++j) y[j] = 0.f;
+  for (int k = 0; k < d; ++k) {
+    const float c = p[k] - pca[k];
+    tot += c * c;
+    for (int j = 0; j < kKeyDims; ++j) y[j] += c * pca[(1 + j) * S + k];
+  }
+  float cap = 0.f;
+  for (int j = 0; j < kKeyDims; ++j) cap += y[j] * y[j];
+  *r2 = tot - cap;
+}
+
 // Global min/max of the first KD coordinates of the real points
 // (lohi: KD minima, then KD maxima, order-encoded).
 __global__ void k_bbox(const float* __restrict__ pts, int64_t n, int S, int KD,
+                       int d, const float* __restrict__ pca,
                        unsigned* __restrict__ lohi) {
   unsigned lo[kKeyDims], hi[kKeyDims];
   for (int k = 0; k < kKeyDims; ++k) {
@@ -57,8 +204,10 @@ __global__ void k_bbox(const float* __restrict__ pts, int64_t n, int S, int KD,
   }
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
+    float y[kKeyDims], r2;
+    key_coords(pts + i * S, KD, d, S, pca, y, &r2);
     for (int k = 0; k < KD; ++k) {
-      const unsigned u = ord_u(pts[i * S + k]);
+      const unsigned u = ord_u(y[k]);
       lo[k] = u < lo[k] ? u : lo[k];
       hi[k] = u > hi[k] ? u : hi[k];
     }
@@ -106,7 +255,8 @@ __device__ __forceinline__ unsigned spread2(unsigned v) {
 // 5 for 6.  Padding rows get the largest key (they sort last, after every
 // real point).
 __global__ void k_keys(const float* __restrict__ pts, int64_t n, int64_t n_pad,
-                       int S, int KD, const unsigned* __restrict__ lohi,
+                       int S, int KD, int d, const float* __restrict__ pca,
+                       const unsigned* __restrict__ lohi,
                        unsigned* __restrict__ keys, int* __restrict__ idx) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -117,11 +267,13 @@ __global__ void k_keys(const float* __restrict__ pts, int64_t n, int64_t n_pad,
       } else {
         const int bits = 30 / KD;
         const float cells = (float)((1 << bits) - 1);
+        float y[kKeyDims], r2;
+        key_coords(pts + i * S, KD, d, S, pca, y, &r2);
         unsigned q[kKeyDims];
         for (int k = 0; k < KD; ++k) {
           const float lo = ord_f(lohi[k]), hi = ord_f(lohi[KD + k]);
           const float span = hi - lo;
-          float f = span > 0.f ? (pts[i * S + k] - lo) / span * cells : 0.f;
+          float f = span > 0.f ? (y[k] - lo) / span * cells : 0.f;
           f = f < 0.f ? 0.f : (f > cells ? cells : f);
           q[k] = (unsigned)f;
         }
@@ -135,6 +287,8 @@ __global__ void k_keys(const float* __restrict__ pts, int64_t n, int64_t n_pad,
           for (int b = 0; b < bits; ++b)
             for (int k = 0; k < KD; ++k)
               key |= ((q[k] >> b) & 1u) << (KD * b + k);
+          // far off the principal directions: after every point near them
+          if (pca != nullptr && r2 > pca[(1 + kKeyDims) * S]) key |= 1u << 31;
         }
       }
     }
@@ -250,12 +404,16 @@ size_t prune_sort_bytes(int64_t n_pad) {
 hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s) {
   // wide points: six key coordinates separate the blocks better than three
   // (measured on 64-d embedded blobs: 30% fewer block pairs kept)
-  const int KD = L.d >= 16 ? kKeyDims : (L.d < 3 ? L.d : 3);
+  const bool wide = L.d >= 16;
+  const int KD = wide ? kKeyDims : (L.d < 3 ? L.d : 3);
+  const float* pca = wide ? L.pca : nullptr;
+  if (wide) k_pca<<<1, 256, 0, s>>>(L.pts, L.n, L.stride, L.d, L.pca);
   k_bbox_init<<<1, 64, 0, s>>>(L.bbox, KD);
   k_bbox<<<grid_for_p(L.n, 256 * 16), 256, 0, s>>>(L.pts, L.n, L.stride, KD,
-                                                   L.bbox);
+                                                   L.d, pca, L.bbox);
   k_keys<<<grid_for_p(L.n_pad, 256 * 4), 256, 0, s>>>(
-      L.pts, L.n, L.n_pad, L.stride, KD, L.bbox, L.keys_in, L.idx_in);
+      L.pts, L.n, L.n_pad, L.stride, KD, L.d, pca, L.bbox, L.keys_in,
+      L.idx_in);
   size_t bytes = L.sort_tmp_bytes;
   hipError_t e = rocprim::radix_sort_pairs(
       L.sort_tmp, bytes, L.keys_in, L.keys_out, L.idx_in, L.perm,
