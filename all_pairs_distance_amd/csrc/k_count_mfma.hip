@@ -85,10 +85,11 @@ __device__ __forceinline__ bool wave_expanded_within(
   return s - inner <= eps2;
 }
 
-// waves per SIMD the register budget is held to (the widths listed fit
-// three without spilling)
+// waves per SIMD the register budget is held to: three from width 24 (at
+// 48 and 64 without the next block's operands in flight, which frees the
+// registers for the third wave; measured faster at 262k x 64)
 constexpr int mfma_waves(int D, bool edges) {
-  return D == 24 || D == 32 ? 3 : 2;
+  return D >= 24 ? 3 : 2;
 }
 
 template <int D, bool EDGES, bool PRUNED>
@@ -109,6 +110,9 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
   constexpr int KQ = D / 4;    // dims per lane group, one per instruction
   constexpr int NG = 4 * P;    // groups of 16 columns per wave
   static_assert(D % 4 == 0 && NG * 16 == 64 * P && NG <= 8, "matrix-core layout");
+  // the next 16-row block's A operand and thresholds are loaded during
+  // the current block (widths below 48)
+  constexpr bool kPrefetch = D < 48;
   // bits 4g + r of a lane's pair mask that belong to row r
   constexpr unsigned kRowBits = NG == 8 ? 0x11111111u : 0x1111u;
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
@@ -160,7 +164,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
     // requested while the current block is on the matrix cores
     float a_next[KQ];
     float2 th_next[4];
-    {
+    if (kPrefetch) {
       const float* ap = srow + (row0 + l16) * SR + q * KQ;
 #pragma unroll
       for (int k = 0; k < KQ; ++k) a_next[k] = ap[k];
@@ -181,11 +185,20 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
       // hi) of this lane's rows rbase + 4q + r
       float a[KQ];
       float2 th[4];
+      if (!kPrefetch) {
+        const float* ap = srow + (rbase + l16) * SR + q * KQ;
 #pragma unroll
-      for (int k = 0; k < KQ; ++k) a[k] = a_next[k];
+        for (int k = 0; k < KQ; ++k) a[k] = ap[k];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) th[r] = th_next[r];
-      if (rb + 16 < rows) {
+        for (int r = 0; r < 4; ++r)
+          th[r] = *(const float2*)(srow + (rbase + 4 * q + r) * SR + D);
+      } else {
+#pragma unroll
+        for (int k = 0; k < KQ; ++k) a[k] = a_next[k];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) th[r] = th_next[r];
+      }
+      if (kPrefetch && rb + 16 < rows) {
         const float* ap = srow + (rbase + 16 + l16) * SR + q * KQ;
 #pragma unroll
         for (int k = 0; k < KQ; ++k) a_next[k] = ap[k];
