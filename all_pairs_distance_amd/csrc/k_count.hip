@@ -242,8 +242,10 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
             }
           }
         }
+        // lane l of rowv holds row l's count; rows without a candidate
+        // leave it at the 0 it started from
+        rowv = write_lane(rowv, (int)acc, l);
       }
-      rowv = write_lane(rowv, (int)acc, l);
     }
     if (rowv) {
       const int64_t r = row0 + rb + lane;
