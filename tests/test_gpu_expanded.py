@@ -40,6 +40,12 @@ def apd():
 def test_expanded_small_and_far_sets(apd, orc, flags, mode):
     disagree = 0
     cases = pins.small_cases(seed=131, count=50) + pins.far_cases(seed=137, count=40)
+    # wide points (the matrix-core pass), near and far from the origin
+    for d, off in ((33, 0.0), (48, 50.0), (64, 10.0)):
+        x = datagen.gaussian_blobs(3000, d, seed=900 + d, n_blobs=6, sigma=0.04,
+                                   noise_frac=0.1)
+        cases.append(((x + np.float32(off)).astype(np.float32),
+                      0.05 * float(np.sqrt(d)), 4))
     for t, (x, eps, m) in enumerate(cases):
         want_l, want_c, _ = orc.fit(x, eps, m, form="expanded")
         lab, cnt, info = gpu_fit(apd, x, eps, m, flags=flags)

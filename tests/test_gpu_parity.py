@@ -357,9 +357,12 @@ def test_schedule_shake(apd, orc):
                                      noise_frac=0.1), 0.012, 6)]
     x2, e2, m2, _ = datagen.make_workload(2)
     cases.append((x2, e2, m2))
+    # wide points: the screened pass runs on the matrix cores
+    cases.append((datagen.gaussian_blobs(9000, 48, seed=19, n_blobs=8,
+                                         sigma=0.05, noise_frac=0.1), 0.45, 5))
     for x, eps, m in cases:
         want_l, want_c, _ = orc.fit(x, eps, m)
-        for base in (0, 2, 4, 8):
+        for base in (0, 2, 4, 8, 12):
             for fl in (base, base | 0x10):
                 lab, cnt, _ = gpu_fit(apd, x, eps, m, flags=fl)
                 assert_same(lab, cnt, want_l, want_c, f"n={x.shape} flags={fl}")
