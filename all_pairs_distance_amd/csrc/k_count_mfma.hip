@@ -10,7 +10,7 @@
 
 namespace dbk {
 
-// Same decisions as the screened pass above, with the screen value
+// The screen value
 //   v = n_y + sum_k (-2 x_k) y_k
 // of a 16-row block against the wave's 64*P columns formed by
 // v_mfma_f32_16x16x4_f32: the rows (pre-scaled by -2) are the A operand,
@@ -21,7 +21,9 @@ namespace dbk {
 // and column value arrives through vector loads: no scalar load per row.
 // The thresholds of this path are widened for the matrix unit's
 // unspecified summation order, rounding and subnormal handling
-// (k_screen.hip); undecided pairs take the exact distance, per lane.
+// (k_screen.hip).  Undecided pairs take the exact distance (or the exact
+// hoisted-norm form): one pair at a time across the wave when a block
+// has a few, per lane when it has many.
 typedef float mf4 __attribute__((ext_vector_type(4)));
 
 // Sum over each 16-lane row of the wave; every lane gets its row's total.
