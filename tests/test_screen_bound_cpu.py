@@ -12,7 +12,9 @@ the screen settles must agree with it.
 For the screen on the matrix cores (widths 16 and up), whose summation
 order, product rounding and rounding mode are not specified, the screen
 value is formed under several such models, each exactly, against the
-widened thresholds of that path.
+widened thresholds of that path.  With the hoisted-norm form as the
+decision, the thresholds of that mode are checked against that form's
+exact value (pins.exact_expanded_rounded) the same way.
 """
 import math
 from fractions import Fraction
@@ -55,7 +57,11 @@ def round_up32(v):
     return f
 
 
-def thresholds(x2, Y, eps2, D, kap_scale=1.0, matrix=False):
+def thresholds(x2, Y, eps2, D, kap_scale=1.0, matrix=False, expanded=False,
+               form_scale=1.0):
+    """lo and hi of one row as the screen-table kernel computes them; with
+    `expanded` for the hoisted-norm form as the decision (its own error
+    term scaled by form_scale)."""
     u, t = 2.0 ** -24, 2.0 ** -149
     gD = D * u / (1 - D * u)
     g2 = (D + 2) * u / (1 - (D + 2) * u)
@@ -63,6 +69,11 @@ def thresholds(x2, Y, eps2, D, kap_scale=1.0, matrix=False):
     kap = (u + 2.01 * (gM if matrix else gD)) * kap_scale
     flush = (2 * D + 2) * 2.0 ** -126 * (1 + 2 * math.sqrt(Y)) * kap_scale if matrix else 0.0
     e2 = float(eps2)
+    if expanded:
+        kapE = (u + 2.01 * gD) * form_scale
+        m = (kap + kapE) * (x2 + Y) + 4 * (D + 1) * t + flush + 1e-12 * (e2 + x2 + Y)
+        return (round_down32(e2 - x2 - m),
+                round_up32(e2 * (1 + 2 * u) + 2 * t - x2 + m))
     L = (e2 - (D + 2) * t) / (1 + g2)
     H = (e2 + (D + 2) * t) / (1 - g2)
     m = kap * (x2 + Y) + (D + 1) * t + flush + 1e-12 * (abs(L) + abs(H) + x2 + Y)
@@ -138,19 +149,24 @@ def matrix_screen_value(x, y, D, mode, fused, order):
     return acc
 
 
-def check_pairs(pairs, eps, D, kap_scale=1.0, model=None):
+def check_pairs(pairs, eps, D, kap_scale=1.0, model=None, expanded=False,
+                form_scale=1.0):
     eps2 = pins.eps2_of(eps)
     # the set's largest squared norm, as the first screen kernel finds it
     Y = max(max(sq_norm64(x), sq_norm64(y)) for x, y in pairs)
     settled = {"in": 0, "out": 0, "exact": 0, "wrong": 0}
     for x, y in pairs:
         lo, hi = thresholds(sq_norm64(x), Y, eps2, D, kap_scale,
-                            matrix=model is not None)
+                            matrix=model is not None, expanded=expanded,
+                            form_scale=form_scale)
         if model is None:
             v = screen_value(x, y)
         else:
             v = np.float32(float(matrix_screen_value(x, y, D, *model)))
-        exact = pins.exact_d2_rounded(x, y) <= eps2
+        if expanded:
+            exact = pins.exact_expanded_rounded(x, y) <= eps2
+        else:
+            exact = pins.exact_d2_rounded(x, y) <= eps2
         if v <= lo:
             settled["in"] += 1
             settled["wrong"] += not exact
@@ -224,4 +240,41 @@ def test_matrix_bound_without_the_rounding_terms_is_caught():
         for model in MODELS:
             wrong += check_pairs(pairs, eps, compiled_width(d), kap_scale=0.0,
                                  model=model)["wrong"]
+    assert wrong > 0
+
+
+# The hoisted-norm form as the decision (DBSCAN_FLAG_EXPANDED): the same
+# screen values against thresholds that bracket that form's own exact
+# decision, which differs from the direct one near the radius.
+EXPANDED_CASES = [(1, 1.0, 0.01), (3, 1.0, 0.003), (3, 100.0, 0.05),
+                  (3, 1e4, 2.0), (8, 1.0, 0.05), (16, 3.0, 0.2), (64, 1.0, 0.35),
+                  (64, 30.0, 1.0)]
+
+
+@pytest.mark.parametrize("d,scale,eps", EXPANDED_CASES)
+def test_expanded_form_decisions(d, scale, eps):
+    rng = np.random.default_rng(9000 + 1000 * d + int(scale))
+    pairs = near_radius_pairs(rng, d, scale, eps, 150 if d < 32 else 60)
+    D = compiled_width(d)
+    models = [None] if D < 16 else [("rn", True, "seq"), ("rz", False, "rev"),
+                                    ("rd", False, "tree")]
+    for model in models:
+        settled = check_pairs(pairs, eps, D, model=model, expanded=True)
+        assert settled["wrong"] == 0, (model, settled)
+        assert settled["exact"] > 0, (model, settled)
+        if scale <= 3.0:
+            assert settled["in"] > 1 and settled["out"] > 0, (model, settled)
+
+
+def test_expanded_bound_without_rounding_terms_is_caught():
+    """Thresholds with neither the screen's nor the form's rounding term
+    settle some pair the wrong way, so the pairs do probe the bracket.
+    (Dropping only the form's term is not caught here: on these pairs the
+    screen's own worst-case term already covers the form's actual error.)"""
+    wrong = 0
+    for d, scale, eps in EXPANDED_CASES:
+        rng = np.random.default_rng(9000 + 1000 * d + int(scale))
+        pairs = near_radius_pairs(rng, d, scale, eps, 150 if d < 32 else 60)
+        wrong += check_pairs(pairs, eps, compiled_width(d), kap_scale=0.0,
+                             expanded=True, form_scale=0.0)["wrong"]
     assert wrong > 0
