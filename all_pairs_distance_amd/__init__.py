@@ -16,7 +16,7 @@ import numpy as np
 
 _C_NAMES = {
     "FLAG_FORCE_TILE_MERGE", "FLAG_PRUNE_TILES", "FLAG_SCREEN",
-    "FLAG_REVERSE_SCHEDULE", "FLAG_EXPANDED",
+    "FLAG_REVERSE_SCHEDULE", "FLAG_EXPANDED", "FLAG_SHUFFLE_SCHEDULE",
     "FLAG_TIME_PHASES", "MAX_D",
     "MERGE_EDGES",
     "MERGE_NONE", "MERGE_TILES", "dbscan_abi_version", "dbscan_fit",

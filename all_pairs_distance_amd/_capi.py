@@ -28,6 +28,7 @@ FLAG_PRUNE_TILES = 0x4
 FLAG_SCREEN = 0x8
 FLAG_REVERSE_SCHEDULE = 0x10
 FLAG_EXPANDED = 0x20
+FLAG_SHUFFLE_SCHEDULE = 0x40
 MAX_D = 64
 
 

@@ -3,6 +3,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <numeric>
 
 #include "dbscan.h"
 #include "internal.h"
@@ -122,6 +123,17 @@ bool carve(Layout& L, void* ws, size_t ws_bytes) {
   return true;
 }
 
+WalkArgs walk_args(Walk w, int64_t count) {
+  if (w.seed == 0 || count <= 1) return WalkArgs{1, 0};
+  if (w.seed == 1) return WalkArgs{-1, count - 1};
+  // a multiplier in [3, 2^14) coprime with count, and an offset, from the
+  // seed (a fixed bijection of 0 .. count-1)
+  const uint64_t h = (uint64_t)w.seed * 0x9E3779B97F4A7C15ull;
+  int64_t mul = 3 + (int64_t)((h >> 20) % 16000u);
+  while (std::gcd(mul, count) != 1) mul = mul + 1 < 16384 ? mul + 1 : 3;
+  return WalkArgs{mul, (int64_t)((h >> 7) % (uint64_t)count)};
+}
+
 }  // namespace dbk
 
 using namespace dbk;
@@ -133,7 +145,8 @@ constexpr uint32_t kKnownFlags = DBSCAN_FLAG_TIME_PHASES |
                                   DBSCAN_FLAG_PRUNE_TILES |
                                   DBSCAN_FLAG_SCREEN |
                                   DBSCAN_FLAG_REVERSE_SCHEDULE |
-                                  DBSCAN_FLAG_EXPANDED;
+                                  DBSCAN_FLAG_EXPANDED |
+                                  DBSCAN_FLAG_SHUFFLE_SCHEDULE;
 
 int check_args(int64_t n, int32_t d, float eps, int32_t min_pts) {
   if (n < 0 || n > (int64_t)INT32_MAX) return DBSCAN_ERR_INVALID_ARG;
@@ -274,7 +287,13 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   if (info) std::memset(info, 0, sizeof(*info));
   int st = check_args(n, d, eps, min_pts);
   if (st != DBSCAN_OK) return st;
-  if (flags & ~kKnownFlags) return DBSCAN_ERR_INVALID_ARG;
+  // bits 16..31 carry the shuffle's seed, and only with the shuffle flag
+  if ((flags & 0xffffu) & ~kKnownFlags) return DBSCAN_ERR_INVALID_ARG;
+  if ((flags >> 16) && !(flags & DBSCAN_FLAG_SHUFFLE_SCHEDULE))
+    return DBSCAN_ERR_INVALID_ARG;
+  if ((flags & DBSCAN_FLAG_SHUFFLE_SCHEDULE) &&
+      (flags & DBSCAN_FLAG_REVERSE_SCHEDULE))
+    return DBSCAN_ERR_INVALID_ARG;
   if ((flags & DBSCAN_FLAG_EXPANDED) && (flags & DBSCAN_FLAG_PRUNE_TILES))
     return DBSCAN_ERR_INVALID_ARG;
   if (n > 0 && (d_points == nullptr || d_labels == nullptr))
@@ -302,7 +321,9 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   const bool prune = (flags & DBSCAN_FLAG_PRUNE_TILES) != 0;
   // the hoisted-norm form is always evaluated behind the screen
   const bool screen = (flags & (DBSCAN_FLAG_SCREEN | DBSCAN_FLAG_EXPANDED)) != 0;
-  const bool reverse = (flags & DBSCAN_FLAG_REVERSE_SCHEDULE) != 0;
+  const Walk walk{(flags & DBSCAN_FLAG_REVERSE_SCHEDULE)   ? 1u
+                  : (flags & DBSCAN_FLAG_SHUFFLE_SCHEDULE) ? 2u + (flags >> 16)
+                                                           : 0u};
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
   int64_t pass1 = 0, pass2 = 0;
 
@@ -312,7 +333,7 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   if (screen)
     DB_TRY(launch_screen(L, prune ? L.sorted_pts : L.pts, eps2, stream));
   tm.mark(1);
-  DB_TRY(launch_count(L, eps2, want_edges, prune, screen, reverse, stream,
+  DB_TRY(launch_count(L, eps2, want_edges, prune, screen, walk, stream,
                       &pass1));
   tm.mark(2);
   DB_TRY(launch_core(L, min_pts, d_counts, stream));
@@ -337,9 +358,9 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   tm.mark(3);
   if (n_core > 0) {
     if (edges_ok)
-      DB_TRY(launch_merge_edges(L, host_st.n_edges, reverse, stream));
+      DB_TRY(launch_merge_edges(L, host_st.n_edges, walk, stream));
     else
-      DB_TRY(launch_merge_tiles(L, eps2, n_core, reverse, stream, &pass2));
+      DB_TRY(launch_merge_tiles(L, eps2, n_core, walk, stream, &pass2));
   }
   tm.mark(4);
   DB_TRY(launch_label(L, d_labels, stream));
@@ -508,7 +529,7 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   if (screen)
     DB_TRY(launch_screen(L, prune ? L.sorted_pts : L.pts, eps2, stream));
   tm.mark(1);
-  DB_TRY(launch_count(L, eps2, true, prune, screen, false, stream, &pass1));
+  DB_TRY(launch_count(L, eps2, true, prune, screen, Walk{0}, stream, &pass1));
   tm.mark(2);
   DB_TRY(launch_row_offsets(L, G, d_row_ptr, d_col_idx, col_cap, stream));
   Status host_st;

@@ -43,6 +43,42 @@ __device__ __forceinline__ float expanded_d2(const float* a, const float* b,
   return s - inner;
 }
 
+// Item visited at step `step` of `count` under a walk (mul, add); see the
+// Walk type.  Products stay below 2^63: |mul| < 2^14 and count < 2^49.
+__device__ __forceinline__ int64_t walk_item(int64_t step, int64_t count,
+                                             int64_t mul, int64_t add) {
+  if (mul == 1) return step;
+  const int64_t v = (mul * step + add) % count;
+  return v < 0 ? v + count : v;
+}
+
+// The same walk re-fitted to another count (a pruned launch learns its
+// item count on the device): reverse stays reverse, a shuffle moves to the
+// next multiplier coprime with the new count.
+__device__ __forceinline__ void walk_refit(int64_t count, int64_t& mul,
+                                           int64_t& add) {
+  if (mul == 1 || count <= 1) {
+    mul = 1;
+    add = 0;
+    return;
+  }
+  if (mul == -1) {
+    add = count - 1;
+    return;
+  }
+  for (;;) {
+    int64_t a = mul, b = count;
+    while (b != 0) {
+      const int64_t r = a % b;
+      a = b;
+      b = r;
+    }
+    if (a == 1) break;
+    mul = mul + 1 < 16384 ? mul + 1 : 3;
+  }
+  add %= count;
+}
+
 // Read-only global memory seen through the constant address space: loads
 // from wave-uniform addresses through such a pointer become scalar loads.
 typedef const float __attribute__((address_space(4)))* const_float_ptr;

@@ -109,17 +109,30 @@ struct GraphLayout {
 size_t layout_min_bytes(int64_t n, int d);
 bool carve(Layout& L, void* ws, size_t ws_bytes);
 
+// The order in which a launch walks its work: a test mode whose results
+// must not change.  Work item `step` of `count` is item
+// (mul * step + add) mod count: mul = 1 walks in order, mul = -1 (add =
+// count - 1) in reverse, other multipliers (below 2^14, coprime with
+// count) a fixed shuffle.
+struct Walk {
+  uint32_t seed;  // 0: in order; 1: reverse; otherwise a shuffle
+};
+struct WalkArgs {
+  int64_t mul, add;
+};
+WalkArgs walk_args(Walk w, int64_t count);
+
 // ---- launchers (each enqueues on `s` and returns hipGetLastError) -------
 hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s);
 hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
-                        bool screen, bool reverse, hipStream_t s,
+                        bool screen, Walk walk, hipStream_t s,
                         int64_t* pairs);
 // The screened count pass runs on the matrix cores for these widths
 // (launch_count_mfma); its thresholds are then widened for the matrix
 // unit's arithmetic.
 constexpr bool screen_on_matrix_cores(int D) { return D >= 16; }
 hipError_t launch_count_mfma(const Layout& L, float eps2, bool edges,
-                             bool pruned, bool reverse, hipStream_t s,
+                             bool pruned, Walk walk, hipStream_t s,
                              int64_t* pairs);
 hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
                          hipStream_t s);
@@ -129,9 +142,9 @@ hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
                        hipStream_t s);
 hipError_t launch_compact(const Layout& L, hipStream_t s);
 hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
-                              bool reverse, hipStream_t s);
+                              Walk walk, hipStream_t s);
 hipError_t launch_merge_tiles(const Layout& L, float eps2, int64_t n_core,
-                              bool reverse, hipStream_t s, int64_t* pairs);
+                              Walk walk, hipStream_t s, int64_t* pairs);
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);
 size_t graph_sort_bytes(int64_t n);
 hipError_t launch_row_offsets(const Layout& L, const GraphLayout& G,

@@ -273,7 +273,7 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     unsigned long long tile_cap, const int* __restrict__ perm,
     const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
     const float* __restrict__ srow, const float* __restrict__ ncol,
-    const float* __restrict__ nexp, int reverse) {
+    const float* __restrict__ nexp, WalkArgs walk) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int SR = screen_stride(D);
@@ -292,11 +292,13 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     if (kept <= tile_cap) {
       items = (int64_t)kept << chunks_log2;
       from_list = true;
+      walk_refit(items, walk.mul, walk.add);
     }
   }
   for (int64_t step = blockIdx.x; step < items; step += gridDim.x) {
-    // (a test mode walks the items in reverse: results must not change)
-    const int64_t item = reverse ? items - 1 - step : step;
+    // (a test mode walks the items in another order: results must not
+    // change)
+    const int64_t item = walk_item(step, items, walk.mul, walk.add);
     const int64_t tile = item >> chunks_log2;
     const int c = (int)(item & ((1 << chunks_log2) - 1));
     int64_t I, J;
@@ -323,7 +325,7 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
 
 template <int D>
 static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
-                                 bool pruned, bool screen, bool reverse,
+                                 bool pruned, bool screen, Walk walk,
                                  hipStream_t s, int64_t* pairs) {
   const CountPlan c = plan_count(L.n_pad, 256 * lane_points(D), pruned);
   const float* pts = pruned ? L.sorted_pts : L.pts;
@@ -333,7 +335,7 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
       L.boxes_w, L.srow, L.ncol, screen && L.expanded ? L.nexp : nullptr,   \
-      reverse ? 1 : 0
+      walk_args(walk, c.items)
 #define DBK_LAUNCH(E, PR, SC) \
   k_count<D, E, PR, SC><<<c.grid, kThreads, 0, s>>>(DBK_COUNT_ARGS)
   if (screen) {
@@ -356,14 +358,14 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
 }
 
 hipError_t launch_count(const Layout& L, float eps2, bool edges, bool pruned,
-                        bool screen, bool reverse, hipStream_t s,
+                        bool screen, Walk walk, hipStream_t s,
                         int64_t* pairs) {
   if (screen && screen_on_matrix_cores(L.D))
-    return launch_count_mfma(L, eps2, edges, pruned, reverse, s, pairs);
+    return launch_count_mfma(L, eps2, edges, pruned, walk, s, pairs);
   switch (L.D) {
 #define DBK_CASE(DD)                                                        \
   case DD:                                                                  \
-    return launch_count_d<DD>(L, eps2, edges, pruned, screen, reverse, s,   \
+    return launch_count_d<DD>(L, eps2, edges, pruned, screen, walk, s,      \
                               pairs);
     DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
     DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)

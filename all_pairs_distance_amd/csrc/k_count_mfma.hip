@@ -104,7 +104,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
     unsigned long long tile_cap, const int* __restrict__ perm,
     const float* __restrict__ srow, const float* __restrict__ ncol,
-    const float* __restrict__ nexp, int reverse) {
+    const float* __restrict__ nexp, WalkArgs walk) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
@@ -130,10 +130,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
     if (kept <= tile_cap) {
       items = (int64_t)kept << chunks_log2;
       from_list = true;
+      walk_refit(items, walk.mul, walk.add);
     }
   }
   for (int64_t step = blockIdx.x; step < items; step += gridDim.x) {
-    const int64_t item = reverse ? items - 1 - step : step;
+    const int64_t item = walk_item(step, items, walk.mul, walk.add);
     const int64_t tile = item >> chunks_log2;
     const int c = (int)(item & ((1 << chunks_log2) - 1));
     int64_t I, J;
@@ -380,7 +381,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
 
 template <int D>
 static hipError_t launch_count_mfma_d(const Layout& L, float eps2, bool edges,
-                                      bool pruned, bool reverse, hipStream_t s,
+                                      bool pruned, Walk walk, hipStream_t s,
                                       int64_t* pairs) {
   const CountPlan c = plan_count(L.n_pad, 256 * lane_points(D), pruned);
   const float* pts = pruned ? L.sorted_pts : L.pts;
@@ -388,7 +389,7 @@ static hipError_t launch_count_mfma_d(const Layout& L, float eps2, bool edges,
   pts, c.nb, c.chunks_log2, c.rows, c.items, eps2, L.count,                  \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                  \
       &L.status->n_edges, L.tiles, &L.status->n_tiles, L.tile_cap, L.perm,   \
-      L.srow, L.ncol, L.expanded ? L.nexp : nullptr, reverse ? 1 : 0
+      L.srow, L.ncol, L.expanded ? L.nexp : nullptr, walk_args(walk, c.items)
   if (edges && pruned)
     k_count_mfma<D, true, true><<<c.grid, kThreads, 0, s>>>(DBK_MFMA_ARGS);
   else if (edges)
@@ -403,14 +404,14 @@ static hipError_t launch_count_mfma_d(const Layout& L, float eps2, bool edges,
 }
 
 hipError_t launch_count_mfma(const Layout& L, float eps2, bool edges,
-                             bool pruned, bool reverse, hipStream_t s,
+                             bool pruned, Walk walk, hipStream_t s,
                              int64_t* pairs) {
   switch (L.D) {
-    case 16: return launch_count_mfma_d<16>(L, eps2, edges, pruned, reverse, s, pairs);
-    case 24: return launch_count_mfma_d<24>(L, eps2, edges, pruned, reverse, s, pairs);
-    case 32: return launch_count_mfma_d<32>(L, eps2, edges, pruned, reverse, s, pairs);
-    case 48: return launch_count_mfma_d<48>(L, eps2, edges, pruned, reverse, s, pairs);
-    case 64: return launch_count_mfma_d<64>(L, eps2, edges, pruned, reverse, s, pairs);
+    case 16: return launch_count_mfma_d<16>(L, eps2, edges, pruned, walk, s, pairs);
+    case 24: return launch_count_mfma_d<24>(L, eps2, edges, pruned, walk, s, pairs);
+    case 32: return launch_count_mfma_d<32>(L, eps2, edges, pruned, walk, s, pairs);
+    case 48: return launch_count_mfma_d<48>(L, eps2, edges, pruned, walk, s, pairs);
+    case 64: return launch_count_mfma_d<64>(L, eps2, edges, pruned, walk, s, pairs);
     default: return hipErrorInvalidValue;
   }
 }

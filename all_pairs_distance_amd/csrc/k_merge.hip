@@ -30,12 +30,14 @@ __global__ void k_merge_edges(const uint2* __restrict__ edges,
                               unsigned long long ne,
                               const unsigned char* __restrict__ core,
                               int* parent, int* __restrict__ bmin,
-                              int reverse) {
+                              WalkArgs walk) {
   for (unsigned long long k = blockIdx.x * (unsigned long long)blockDim.x +
                               threadIdx.x;
        k < ne; k += (unsigned long long)gridDim.x * blockDim.x) {
-    // (a test mode walks the pairs in reverse: results must not change)
-    const unsigned long long e = reverse ? ne - 1 - k : k;
+    // (a test mode walks the pairs in another order: results must not
+    // change)
+    const unsigned long long e =
+        (unsigned long long)walk_item((int64_t)k, (int64_t)ne, walk.mul, walk.add);
     const uint2 ij = edges[e];
     const int i = (int)ij.x, j = (int)ij.y;
     const bool ci = core[i] != 0, cj = core[j] != 0;
@@ -49,12 +51,13 @@ __global__ void k_merge_edges(const uint2* __restrict__ edges,
 }
 
 hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
-                              bool reverse, hipStream_t s) {
+                              Walk walk, hipStream_t s) {
   if (n_edges == 0) return hipSuccess;
   unsigned long long g = (n_edges + 255) / 256;
   if (g > (unsigned long long)kMaxGrid) g = kMaxGrid;
   k_merge_edges<<<(unsigned)g, 256, 0, s>>>(L.edges, n_edges, L.core,
-                                            L.parent, L.bmin, reverse ? 1 : 0);
+                                            L.parent, L.bmin,
+                                            walk_args(walk, (int64_t)n_edges));
   return hipGetLastError();
 }
 
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     const int* __restrict__ core_list, const unsigned char* __restrict__ core,
     int64_t row_blocks, int64_t col_blocks, float eps2, int* parent,
     int* __restrict__ bmin, const float* __restrict__ nexp, int64_t n_core,
-    int reverse) {
+    WalkArgs walk_r, WalkArgs walk_c) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
@@ -76,9 +79,10 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   for (int64_t rs = blockIdx.y; rs < row_blocks; rs += gridDim.y)
   for (int64_t cs = blockIdx.x; cs < col_blocks; cs += gridDim.x) {
-    // (a test mode walks the blocks in reverse: results must not change)
-    const int64_t rblk = reverse ? row_blocks - 1 - rs : rs;
-    const int64_t cblk = reverse ? col_blocks - 1 - cs : cs;
+    // (a test mode walks the blocks in another order: results must not
+    // change)
+    const int64_t rblk = walk_item(rs, row_blocks, walk_r.mul, walk_r.add);
+    const int64_t cblk = walk_item(cs, col_blocks, walk_c.mul, walk_c.add);
     const int64_t row0 = rblk * kRowsPerItem;
     const int64_t colw = cblk * T + (int64_t)wave * 64 * P;
     float xc[P][D];
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
 
 template <int D>
 static hipError_t launch_merge_tiles_d(const Layout& L, float eps2,
-                                       int64_t n_core, bool reverse,
+                                       int64_t n_core, Walk walk,
                                        hipStream_t s, int64_t* pairs) {
   constexpr int T = 256 * lane_points(D);
   const int64_t nc_pad = (n_core + T - 1) / T * T;
@@ -140,30 +144,32 @@ static hipError_t launch_merge_tiles_d(const Layout& L, float eps2,
   if (L.expanded)
     k_merge_tiles<D, true><<<grid, kThreads, 0, s>>>(
         L.pts, L.core_pts, L.core_list, L.core, row_blocks, col_blocks, eps2,
-        L.parent, L.bmin, L.nexp, n_core, reverse ? 1 : 0);
+        L.parent, L.bmin, L.nexp, n_core, walk_args(walk, row_blocks),
+        walk_args(walk, col_blocks));
   else
     k_merge_tiles<D, false><<<grid, kThreads, 0, s>>>(
         L.pts, L.core_pts, L.core_list, L.core, row_blocks, col_blocks, eps2,
-        L.parent, L.bmin, nullptr, n_core, reverse ? 1 : 0);
+        L.parent, L.bmin, nullptr, n_core, walk_args(walk, row_blocks),
+        walk_args(walk, col_blocks));
   if (pairs) *pairs = L.n_pad * nc_pad;
   return hipGetLastError();
 }
 
 hipError_t launch_merge_tiles(const Layout& L, float eps2, int64_t n_core,
-                              bool reverse, hipStream_t s, int64_t* pairs) {
+                              Walk walk, hipStream_t s, int64_t* pairs) {
   switch (L.D) {
-    case 1: return launch_merge_tiles_d<1>(L, eps2, n_core, reverse, s, pairs);
-    case 2: return launch_merge_tiles_d<2>(L, eps2, n_core, reverse, s, pairs);
-    case 3: return launch_merge_tiles_d<3>(L, eps2, n_core, reverse, s, pairs);
-    case 4: return launch_merge_tiles_d<4>(L, eps2, n_core, reverse, s, pairs);
-    case 6: return launch_merge_tiles_d<6>(L, eps2, n_core, reverse, s, pairs);
-    case 8: return launch_merge_tiles_d<8>(L, eps2, n_core, reverse, s, pairs);
-    case 12: return launch_merge_tiles_d<12>(L, eps2, n_core, reverse, s, pairs);
-    case 16: return launch_merge_tiles_d<16>(L, eps2, n_core, reverse, s, pairs);
-    case 24: return launch_merge_tiles_d<24>(L, eps2, n_core, reverse, s, pairs);
-    case 32: return launch_merge_tiles_d<32>(L, eps2, n_core, reverse, s, pairs);
-    case 48: return launch_merge_tiles_d<48>(L, eps2, n_core, reverse, s, pairs);
-    case 64: return launch_merge_tiles_d<64>(L, eps2, n_core, reverse, s, pairs);
+    case 1: return launch_merge_tiles_d<1>(L, eps2, n_core, walk, s, pairs);
+    case 2: return launch_merge_tiles_d<2>(L, eps2, n_core, walk, s, pairs);
+    case 3: return launch_merge_tiles_d<3>(L, eps2, n_core, walk, s, pairs);
+    case 4: return launch_merge_tiles_d<4>(L, eps2, n_core, walk, s, pairs);
+    case 6: return launch_merge_tiles_d<6>(L, eps2, n_core, walk, s, pairs);
+    case 8: return launch_merge_tiles_d<8>(L, eps2, n_core, walk, s, pairs);
+    case 12: return launch_merge_tiles_d<12>(L, eps2, n_core, walk, s, pairs);
+    case 16: return launch_merge_tiles_d<16>(L, eps2, n_core, walk, s, pairs);
+    case 24: return launch_merge_tiles_d<24>(L, eps2, n_core, walk, s, pairs);
+    case 32: return launch_merge_tiles_d<32>(L, eps2, n_core, walk, s, pairs);
+    case 48: return launch_merge_tiles_d<48>(L, eps2, n_core, walk, s, pairs);
+    case 64: return launch_merge_tiles_d<64>(L, eps2, n_core, walk, s, pairs);
     default: return hipErrorInvalidValue;
   }
 }

@@ -90,6 +90,13 @@ typedef enum dbscan_status {
                                              pairs and the tile merge's
                                              blocks in reverse order; the
                                              results must not change */
+#define DBSCAN_FLAG_SHUFFLE_SCHEDULE 0x40u /* for testing: walk them in a
+                                             fixed shuffled order instead,
+                                             chosen by the seed in bits
+                                             16..31 of the flags (allowed
+                                             only with this flag; not with
+                                             the reverse flag); the results
+                                             must not change */
 #define DBSCAN_FLAG_SCREEN 0x8u /* decide most pairs of the count pass with
                                    the hoisted-norm form |y|^2 - 2 x.y
                                    (Wang et al. Sec. IV-B2) evaluated with

@@ -118,6 +118,7 @@ def test_graph_invalid_arguments_rejected_before_device_work():
     assert _graph_status(x, 8, 2, 0.1, flags=0x80) == bad
     assert _graph_status(x, 8, 2, 0.1, flags=0x10) == bad      # fits only
     assert _graph_status(x, 8, 2, 0.1, flags=0x24) == bad      # expanded + pruned
+    assert _graph_status(x, 8, 2, 0.1, flags=0x40) == bad      # fits only
 
 
 def _status(points, n, d, eps, m, labels=True):
@@ -148,6 +149,10 @@ def test_invalid_arguments_rejected_before_device_work():
                                   _capi.FLAG_EXPANDED | _capi.FLAG_PRUNE_TILES,
                                   None)
     assert st == _capi.ERR_INVALID_ARG   # the pruning bound is for the direct form
+    for fl in (1 << 16, _capi.FLAG_SHUFFLE_SCHEDULE | _capi.FLAG_REVERSE_SCHEDULE):
+        st = apd.dbscan_fit_device_ex(x.ctypes.data, 8, 2, 0.1, 1, ws.ctypes.data,
+                                      None, ws.ctypes.data, 16, None, fl, None)
+        assert st == _capi.ERR_INVALID_ARG   # seed bits need the shuffle flag
 
 
 def _gpu_visible():

@@ -347,10 +347,10 @@ def test_screen_edge_cases(apd, orc, flags, mode):
 
 def test_schedule_shake(apd, orc):
     """Walking the count pass's items, the recorded pairs and the tile
-    merge's blocks in reverse order (and with another edge capacity, which
-    changes which merge runs and the order pairs are recorded in) gives
-    the same labels: the union-find result does not depend on the order
-    of the links."""
+    merge's blocks in reverse order or in seeded shuffled orders (and with
+    another edge capacity, which changes which merge runs and the order
+    pairs are recorded in) gives the same labels: the union-find result
+    does not depend on the order of the links."""
     cases = [(datagen.collinear_chain(20000, 0.5), 0.5, 2),
              (datagen.integer_lattice(120, 2), 1.0, 5),
              (datagen.gaussian_blobs(30000, 3, seed=9, n_blobs=30, sigma=0.01,
@@ -362,8 +362,9 @@ def test_schedule_shake(apd, orc):
                                          sigma=0.05, noise_frac=0.1), 0.45, 5))
     for x, eps, m in cases:
         want_l, want_c, _ = orc.fit(x, eps, m)
+        shuffles = tuple(0x40 | (seed << 16) for seed in (0, 1, 7, 123, 4321, 65535))
         for base in (0, 2, 4, 8, 12):
-            for fl in (base, base | 0x10):
+            for fl in (base, base | 0x10) + tuple(base | sh for sh in shuffles):
                 lab, cnt, _ = gpu_fit(apd, x, eps, m, flags=fl)
                 assert_same(lab, cnt, want_l, want_c, f"n={x.shape} flags={fl}")
         lab, cnt, info = gpu_fit(apd, x, eps, m, flags=0x10, max_edges=1000)
