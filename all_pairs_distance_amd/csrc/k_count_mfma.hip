@@ -17,8 +17,10 @@ namespace dbk {
 // the columns the B operand and the column norms the accumulator's start.
 // Lane l supplies A[l%16][k] and B[k][l%16] for dims k of its lane group
 // q = l/16 (dims q*D/4 .. q*D/4 + D/4 - 1, one per instruction) and holds
-// the results of rows 4q + r (r = 0..3) against column l%16.  Every row
-// and column value arrives through vector loads: no scalar load per row.
+// the results of rows 4q + r (r = 0..3) against column l%16.  Rows come
+// through LDS (64 at a time, copied straight from memory into LDS and
+// shared by the work-group's four waves), columns through vector loads:
+// no scalar load per row.
 // The thresholds of this path are widened for the matrix unit's
 // unspecified summation order, rounding and subnormal handling
 // (k_screen.hip).  Undecided pairs take the exact distance (or the exact
@@ -87,9 +89,24 @@ __device__ __forceinline__ bool wave_expanded_within(
   return s - inner <= eps2;
 }
 
-// waves per SIMD the register budget is held to: three from width 24 (at
-// 48 and 64 without the next block's operands in flight, which frees the
-// registers for the third wave; measured faster at 262k x 64)
+// Copy n4 16-byte words from global memory (src) to LDS (dst) with the
+// work-group's 256 threads, straight into LDS (no registers): word
+// t + 256 j of the copy is lane t % 64 of wave t / 64's j-th load, which
+// writes its 16 bytes at the wave's LDS base + 16 * lane.  Completion is
+// awaited by the caller (vmcnt, then a barrier).
+__device__ __forceinline__ void stage_to_lds(const float* __restrict__ src,
+                                             float* dst, int n4) {
+  const int w = (int)(threadIdx.x >> 6), lane = lane_id();
+  for (int j = 0; j * 256 < n4; ++j) {
+    const int base = j * 256 + w * 64;
+    if (base + lane < n4)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src + (int64_t)(base + lane) * 4),
+          (__attribute__((address_space(3))) void*)(dst + base * 4), 16, 0, 0);
+  }
+}
+
+// waves per SIMD the register budget is held to: three from width 24
 constexpr int mfma_waves(int D, bool edges) {
   return D >= 24 ? 3 : 2;
 }
@@ -112,9 +129,11 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
   constexpr int KQ = D / 4;    // dims per lane group, one per instruction
   constexpr int NG = 4 * P;    // groups of 16 columns per wave
   static_assert(D % 4 == 0 && NG * 16 == 64 * P && NG <= 8, "matrix-core layout");
-  // the next 16-row block's A operand and thresholds are loaded during
-  // the current block (widths below 48)
-  constexpr bool kPrefetch = D < 48;
+  // rows (-2x, lo, hi) reach the waves through LDS, 64 at a time, double
+  // buffered and shared by the work-group's four waves (same rows,
+  // different columns)
+  constexpr int kChunk4 = 16 * SR;   // 16-byte words per 64 rows
+  __shared__ __attribute__((aligned(16))) float rows_lds[2 * 64 * SR];
   // bits 4g + r of a lane's pair mask that belong to row r
   constexpr unsigned kRowBits = NG == 8 ? 0x11111111u : 0x1111u;
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
@@ -163,51 +182,40 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
       lc[g] = 0;
     }
     unsigned rowv = 0;  // lane l: count of row (64-row window) + l
-    // the A operand and the thresholds of the next 16-row block are
-    // requested while the current block is on the matrix cores
-    float a_next[KQ];
-    float2 th_next[4];
-    if (kPrefetch) {
-      const float* ap = srow + (row0 + l16) * SR + q * KQ;
-#pragma unroll
-      for (int k = 0; k < KQ; ++k) a_next[k] = ap[k];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        th_next[r] = *(const float2*)(srow + (row0 + 4 * q + r) * SR + D);
-    }
+    // every wave is done with the previous item's rows before the first
+    // chunk of this one lands
+    __syncthreads();
+    stage_to_lds(srow + row0 * SR, rows_lds, kChunk4);
     for (int rb = 0; rb < rows; rb += 16) {
-      if ((rb & 63) == 0 && rb > 0) {
-        if (rowv) {
-          const int64_t i = row0 + rb - 64 + lane;
-          atomicAdd(count + (PRUNED ? perm[i] : i), rowv);
+      if ((rb & 63) == 0) {
+        if (rb > 0) {
+          if (rowv) {
+            const int64_t i = row0 + rb - 64 + lane;
+            atomicAdd(count + (PRUNED ? perm[i] : i), rowv);
+          }
+          rowv = 0;
         }
-        rowv = 0;
+        // this chunk has landed (and every wave is done with the buffer
+        // the next chunk goes to); start the next chunk
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (rb + 64 < rows)
+          stage_to_lds(srow + (row0 + rb + 64) * SR,
+                       rows_lds + (((rb >> 6) + 1) & 1) * 64 * SR, kChunk4);
       }
       const int64_t rbase = row0 + rb;
+      const float* cur = rows_lds + ((rb >> 6) & 1) * 64 * SR + (rb & 63) * SR;
       // A operand: row rbase + l16, dims of lane group q; thresholds (lo,
       // hi) of this lane's rows rbase + 4q + r
       float a[KQ];
       float2 th[4];
-      if (!kPrefetch) {
-        const float* ap = srow + (rbase + l16) * SR + q * KQ;
+      {
+        const float* ap = cur + l16 * SR + q * KQ;
 #pragma unroll
         for (int k = 0; k < KQ; ++k) a[k] = ap[k];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          th[r] = *(const float2*)(srow + (rbase + 4 * q + r) * SR + D);
-      } else {
-#pragma unroll
-        for (int k = 0; k < KQ; ++k) a[k] = a_next[k];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) th[r] = th_next[r];
-      }
-      if (kPrefetch && rb + 16 < rows) {
-        const float* ap = srow + (rbase + 16 + l16) * SR + q * KQ;
-#pragma unroll
-        for (int k = 0; k < KQ; ++k) a_next[k] = ap[k];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          th_next[r] = *(const float2*)(srow + (rbase + 16 + 4 * q + r) * SR + D);
+          th[r] = *(const float2*)(cur + (4 * q + r) * SR + D);
       }
       mf4 acc[NG];
 #pragma unroll
