@@ -66,8 +66,10 @@ __device__ __forceinline__ void stage_edges(uint64_t m, int64_t row,
 // with the row pre-scaled by -2) is compared with two per-row thresholds
 // that bracket the exact decision by a proven error bound (k_screen.hip).
 // v <= lo: certainly a neighbour; v > hi: certainly not; in between the
-// row's exact distances are evaluated on a rare, wave-uniform path, so the
-// result is bit-identical to the exact pass.
+// row's exact distances (or, with a norm table, the exact hoisted-norm
+// form) are evaluated on a rare, wave-uniform path, so the result is
+// bit-identical to the exact pass (or to that form).  Its row records go
+// through the wave's LDS area, 64 rows at a time, read back as broadcasts.
 template <int D, int P, bool DIAG, bool EDGES, bool PRUNED, bool SCREEN>
 __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            int64_t row0, int rows,
