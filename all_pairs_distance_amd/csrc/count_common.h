@@ -49,6 +49,52 @@ __device__ __forceinline__ void flush_edges(uint2* stage, unsigned fill,
   wave_lds_sync();
 }
 
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ unsigned wave_incl_sum(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const unsigned t0 = (unsigned)__builtin_amdgcn_readlane((int)v, 15);
+  const unsigned t1 = (unsigned)__builtin_amdgcn_readlane((int)v, 31);
+  const unsigned t2 = (unsigned)__builtin_amdgcn_readlane((int)v, 47);
+  const int q = lane_id() >> 4;
+  return v + (q >= 1 ? t0 : 0u) + (q >= 2 ? t1 : 0u) + (q >= 3 ? t2 : 0u);
+}
+
+// Stage captured pairs: lane l contributes one pair per set bit b of its
+// `bits`, pair_of(b) (a uint2 of output indices), and the pairs are packed
+// by a prefix sum over the lanes instead of one ballot scan per column
+// group.  When the pairs outnumber the stage they reserve their slots in
+// the edge area and are written there directly.
+template <typename PairOf>
+__device__ __forceinline__ void stage_pairs(unsigned bits, PairOf pair_of,
+                                            uint2* stage, unsigned& fill,
+                                            const EdgeSink& sink) {
+  const unsigned n_e = (unsigned)__builtin_popcount(bits);
+  const unsigned incl = wave_incl_sum(n_e);
+  const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+  if (total == 0) return;
+  if (fill + total > (unsigned)kEdgeStage) {
+    if (fill) flush_edges(stage, fill, sink);
+    fill = 0;
+  }
+  if (total <= (unsigned)kEdgeStage) {
+    unsigned pos = fill + incl - n_e;
+    for (unsigned w = bits; w != 0; w &= w - 1)
+      stage[pos++] = pair_of(__builtin_ctz(w));
+    fill += total;
+  } else {
+    unsigned long long base = 0;
+    if (lane_id() == 0) base = atomicAdd(sink.counter, (unsigned long long)total);
+    base = uniform_u64(base) + (incl - n_e);
+    for (unsigned w = bits; w != 0; w &= w - 1) {
+      if (base < sink.cap) sink.edges[base] = pair_of(__builtin_ctz(w));
+      ++base;
+    }
+  }
+}
+
 // Work items of a count launch: the upper triangle of nb x nb blocks of T
 // points, each tile cut into chunks of `rows` rows.  A whole block of T
 // rows per item loads each column block once per tile (a pruned launch

@@ -112,6 +112,13 @@ __device__ __forceinline__ unsigned add_lane_bit(unsigned cnt, uint64_t mask) {
   return cnt;
 }
 
+// 2*v + (bit `lane` of mask): shifts this lane's bit of a wave-uniform
+// mask into v, one VALU op (the same add-with-carry as add_lane_bit).
+__device__ __forceinline__ unsigned shift_in_lane_bit(unsigned v, uint64_t mask) {
+  asm("v_addc_co_u32_e64 %0, vcc, %0, %0, %1" : "+v"(v) : "s"(mask) : "vcc");
+  return v;
+}
+
 __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
   unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
   unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));

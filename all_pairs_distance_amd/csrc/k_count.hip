@@ -225,22 +225,48 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
           // recomputed here, on the rare path, instead of P live registers
           asm volatile("" : "+v"(lane_col));
           const int row_out = PRUNED ? ((const_int_ptr)perm)[row] : (int)row;
-          // at most 8 column groups (512 pairs) staged per capacity check
+          if constexpr (P >= 16) {
+            // many groups per row (narrow points, dense rows): collect the
+            // lane's pairs of all groups (group p's bit at position P-1-p)
+            // and pack them with one prefix sum over the lanes
+            unsigned pat = 0;
 #pragma unroll
-          for (int g = 0; g < P; g += 8) {
-            constexpr int G = P < 8 ? P : 8;
-            unsigned want = 0;
-#pragma unroll
-            for (int p = g; p < g + G; ++p) want += (unsigned)__popcll(m[p]);
-            if (fill + want > (unsigned)kEdgeStage) {
-              flush_edges(stage, fill, sink);
-              fill = 0;
+            for (int p = 0; p < P; ++p) pat = shift_in_lane_bit(pat, m[p]);
+            if (DIAG) {
+              // pairs with column > row only (each unordered pair once,
+              // never (i, i)): the lane's column of group p exceeds the
+              // row for p >= p0
+              const int q = (int)(row - colw) - lane;
+              const int p0 = q < 0 ? 0 : (q >> 6) + 1;
+              pat = p0 >= P ? 0u : pat & ((2u << (P - 1 - p0)) - 1u);
             }
+            stage_pairs(
+                pat,
+                [&](int b) {
+                  const int col = lane_col + (P - 1 - b) * 64;
+                  return make_uint2((unsigned)row_out,
+                                    (unsigned)(PRUNED ? perm[col] : col));
+                },
+                stage, fill, sink);
+          } else {
+            // few groups: one ballot scan per group with a pair, at most
+            // 8 groups (512 pairs) per capacity check
 #pragma unroll
-            for (int p = g; p < g + G; ++p) {
-              const int col = lane_col + p * 64;
-              stage_edges<DIAG>(m[p], row, colw + p * 64, row_out,
-                                PRUNED ? perm[col] : col, stage, fill);
+            for (int g = 0; g < P; g += 8) {
+              constexpr int G = P < 8 ? P : 8;
+              unsigned want = 0;
+#pragma unroll
+              for (int p = g; p < g + G; ++p) want += (unsigned)__popcll(m[p]);
+              if (fill + want > (unsigned)kEdgeStage) {
+                flush_edges(stage, fill, sink);
+                fill = 0;
+              }
+#pragma unroll
+              for (int p = g; p < g + G; ++p) {
+                const int col = lane_col + p * 64;
+                stage_edges<DIAG>(m[p], row, colw + p * 64, row_out,
+                                  PRUNED ? perm[col] : col, stage, fill);
+              }
             }
           }
         }
