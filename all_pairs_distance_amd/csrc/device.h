@@ -106,16 +106,21 @@ __device__ __forceinline__ int write_lane(int vgpr, int value, int lane) {
 
 // cnt + (bit `lane` of mask) in one VALU op: v_addc with the wave-uniform
 // mask (an SGPR pair) as the carry-in.  Left to itself the compiler may
-// spend a v_cndmask and a v_add on it.
+// spend a v_cndmask and a v_add on it.  The compiler keeps two wait states
+// between a VALU write of an SGPR pair and a VALU read of it as a lane
+// mask, but cannot see into this asm, and the mask is usually written by a
+// compare just before: the s_nop supplies those two wait states.
 __device__ __forceinline__ unsigned add_lane_bit(unsigned cnt, uint64_t mask) {
-  asm("v_addc_co_u32_e64 %0, vcc, %0, 0, %1" : "+v"(cnt) : "s"(mask) : "vcc");
+  asm("s_nop 1\n\tv_addc_co_u32_e64 %0, vcc, %0, 0, %1"
+      : "+v"(cnt) : "s"(mask) : "vcc");
   return cnt;
 }
 
 // 2*v + (bit `lane` of mask): shifts this lane's bit of a wave-uniform
 // mask into v, one VALU op (the same add-with-carry as add_lane_bit).
 __device__ __forceinline__ unsigned shift_in_lane_bit(unsigned v, uint64_t mask) {
-  asm("v_addc_co_u32_e64 %0, vcc, %0, %0, %1" : "+v"(v) : "s"(mask) : "vcc");
+  asm("s_nop 1\n\tv_addc_co_u32_e64 %0, vcc, %0, %0, %1"
+      : "+v"(v) : "s"(mask) : "vcc");
   return v;
 }
 

@@ -114,3 +114,40 @@ def test_tile_bound_has_no_fused_fp32(asm):
     for name, body in bodies.items():
         assert not FORBIDDEN.findall(body), name
         assert "v_mul_f32" in body and "v_add_f32" in body
+
+
+def _mask_read_too_early(body: str):
+    """Sites where a v_addc_co_u32 reads an SGPR pair as its carry-in less
+    than two wait states after a VALU instruction wrote that pair.  The
+    compiler keeps that distance for the mask reads it schedules itself
+    (v_cndmask, v_addc); hand-written add-with-carry must keep it too."""
+    ins = [l.strip() for l in body.split("\n")]
+    ins = [l for l in ins if l and not l.startswith((";", ".")) and not l.endswith(":")]
+    bad = []
+    for i, line in enumerate(ins):
+        m = re.match(r"v_addc_co_u32_e64 v\d+, vcc, v\d+, (?:v\d+|0), (s\[\d+:\d+\])", line)
+        if not m:
+            continue
+        reg, waits = m.group(1), 0
+        for prev in reversed(ins[max(0, i - 6):i]):
+            if prev.startswith("s_nop"):
+                waits += int(prev.split()[1]) + 1
+                continue
+            if re.match(r"\w+ " + re.escape(reg) + ",", prev):
+                if prev.startswith("v_") and waits < 2:
+                    bad.append((prev, line))
+                break
+            waits += 1
+            if waits >= 2:
+                break
+    return bad
+
+
+def test_lane_mask_reads_keep_two_wait_states(asm):
+    bodies = kernel_bodies(asm["count"], "7k_countI")
+    sites = 0
+    for name, body in bodies.items():
+        sites += body.count("v_addc_co_u32_e64")
+        bad = _mask_read_too_early(body)
+        assert not bad, (name, bad[:2])
+    assert sites > 0
