@@ -14,7 +14,7 @@ namespace dbk {
 //   v = n_y + sum_k (-2 x_k) y_k
 // of a 16-row block against the wave's 64*P columns formed by
 // v_mfma_f32_16x16x4_f32: the rows (pre-scaled by -2) are the A operand,
-// the columns the B operand and the column norms the accumulator's start.
+// the columns the B operand; the column norms are added to the products.
 // Lane l supplies A[l%16][k] and B[k][l%16] for dims k of its lane group
 // q = l/16 (dims q*D/4 .. q*D/4 + D/4 - 1, one per instruction) and holds
 // the results of rows 4q + r (r = 0..3) against column l%16.  Rows come
@@ -206,13 +206,20 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
       }
       mf4 acc[NG];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) acc[g] = mf4{ny[g], ny[g], ny[g], ny[g]};
+      for (int g = 0; g < NG; ++g) acc[g] = mf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KQ; ++k)
 #pragma unroll
         for (int g = 0; g < NG; ++g)
           acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k], bq[g][k], acc[g],
                                                         0, 0, 0);
+      // the column norm joins last: one more rounded addition, an order
+      // the bound allows (any order of the D + 1 terms); starting the
+      // products from zero spares the registers of a replicated norm
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[g][r] = acc[g][r] + ny[g];
       // any candidate neighbour in the block?  (min skips NaN padding)
       float tmin = acc[0][0] - th[0].y;
 #pragma unroll
