@@ -2,6 +2,8 @@
 // the tile enumeration, the edge sink and the wave's LDS edge stage.
 #pragma once
 
+#include <cmath>
+
 #include "device.h"
 #include "internal.h"
 
@@ -93,6 +95,23 @@ __device__ __forceinline__ void stage_pairs(unsigned bits, PairOf pair_of,
       ++base;
     }
   }
+}
+
+// Threshold for wave_boxes_apart.  Let G be the ascending-k fp32 sum of
+// the S squared gaps q_k and W their tree sum (at most 7 additions per
+// term), T the exact sum of the q_k.  Both sums of non-negative terms lie
+// within a relative g_m = m u / (1 - m u) of T: G >= (1 - g_{S-1}) T and
+// W <= (1 + g_7) T, so W > eps2 (1 + g_8) / (1 - g_S) proves G > eps2.
+// Every pair's fp32 distance is at least G (boxes_apart), so the boxes
+// hold no neighbours.  The bound is rounded up to fp32.
+inline float box_gap_threshold(float eps2, int S) {
+  const double u = 0x1p-24;
+  const auto g = [u](double m) { return m * u / (1.0 - m * u); };
+  const double t = (double)eps2 * (1.0 + g(8.0)) / (1.0 - g((double)S)) *
+                   (1.0 + 0x1p-50);
+  float f = (float)t;
+  if ((double)f < t) f = nextafterf(f, __builtin_inff());
+  return f;
 }
 
 // Work items of a count launch: the upper triangle of nb x nb blocks of T

@@ -151,6 +151,48 @@ __device__ __forceinline__ bool boxes_apart(const_float_ptr a, const_float_ptr b
   return s > eps2;
 }
 
+// Sum of v over the 64 lanes, in some fixed tree order (each term passes
+// at most 7 additions); the result is in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm 1,0,3,2
+  v += dpp_f32<0x4E>(v);   // quad_perm 2,3,0,1
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror: every lane holds its 16-lane row's sum
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+// The box test of boxes_apart computed by the whole wave for wide points:
+// lane k forms the rounded square of the rounded gap in dimension k, and
+// the squares are summed in a tree instead of in ascending k.  thr
+// (box_gap_threshold) is eps2 widened so that a tree sum above it proves
+// the ascending-k sum, and so every pair's fp32 distance, above eps2.
+template <int S>
+__device__ __forceinline__ bool wave_boxes_apart(const float* __restrict__ a,
+                                                 const float* __restrict__ b,
+                                                 float thr) {
+  static_assert(S <= 64, "one dimension per lane");
+  const int k = lane_id();
+  float q = 0.f;
+  if (k < S) {
+    const float alo = a[k], ahi = a[S + k], blo = b[k], bhi = b[S + k];
+    float g = 0.f;
+    if (blo > ahi) g = blo - ahi;
+    else if (alo > bhi) g = alo - bhi;
+    q = g * g;
+  }
+  return wave_sum_f32(q) > thr;
+}
+
 // Exclusive prefix sum over a 256-thread (4-wave) block; *total gets the
 // block's sum.  sh: 4 words of LDS.
 __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* sh,

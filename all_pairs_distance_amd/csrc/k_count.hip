@@ -80,6 +80,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            const int* __restrict__ perm,
                                            const float* __restrict__ boxes64,
                                            const float* __restrict__ boxes_w,
+                                           float box_thr,
                                            const float* __restrict__ srow,
                                            const float* __restrict__ ncol,
                                            const float* __restrict__ nexp,
@@ -110,14 +111,17 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 
   for (int rb = 0; rb < rows; rb += 64) {
     // pruned: skip 64 rows whose box is provably farther than eps from
-    // every column point of this wave (no neighbour among them); only for
-    // narrow points, where the test is a few scalar loads and the boxes
-    // are tight
-    if (PRUNED && D <= 16 &&
-        boxes_apart<S>((const_float_ptr)(boxes64 + ((row0 + rb) >> 6) * 2 * S),
-                       (const_float_ptr)(boxes_w + (colw / (64 * P)) * 2 * S),
-                       eps2))
-      continue;
+    // every column point of this wave (no neighbour among them): for
+    // narrow points a few scalar loads in the distance's own order, for
+    // wide ones one dimension per lane with a widened threshold
+    if (PRUNED) {
+      const float* rbox = boxes64 + ((row0 + rb) >> 6) * 2 * S;
+      const float* cbox = boxes_w + (colw / (64 * P)) * 2 * S;
+      if (D <= 16 ? boxes_apart<S>((const_float_ptr)rbox,
+                                   (const_float_ptr)cbox, eps2)
+                  : wave_boxes_apart<S>(rbox, cbox, box_thr))
+        continue;
+    }
     int rowv = 0;  // lane l: count of row rb+l over these columns
     if (SCREEN) {
       // the 64 rows' records (-2x, lo, hi) go to the wave's LDS area with
@@ -300,8 +304,9 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
     unsigned long long tile_cap, const int* __restrict__ perm,
     const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
-    const float* __restrict__ srow, const float* __restrict__ ncol,
-    const float* __restrict__ nexp, WalkArgs walk) {
+    float box_thr, const float* __restrict__ srow,
+    const float* __restrict__ ncol, const float* __restrict__ nexp,
+    WalkArgs walk) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int SR = screen_stride(D);
@@ -342,11 +347,11 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     if (I == J)
       count_item<D, P, true, EDGES, PRUNED, SCREEN>(
           pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, srow, ncol, nexp, rows_lds);
+          boxes_w, box_thr, srow, ncol, nexp, rows_lds);
     else
       count_item<D, P, false, EDGES, PRUNED, SCREEN>(
           pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, srow, ncol, nexp, rows_lds);
+          boxes_w, box_thr, srow, ncol, nexp, rows_lds);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
@@ -362,7 +367,8 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   pts, c.nb, c.chunks_log2, c.rows, c.items, eps2, L.count,                 \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
-      L.boxes_w, L.srow, L.ncol, screen && L.expanded ? L.nexp : nullptr,   \
+      L.boxes_w, box_gap_threshold(eps2, row_stride(D)), L.srow, L.ncol,    \
+      screen && L.expanded ? L.nexp : nullptr,                              \
       walk_args(walk, c.items)
 #define DBK_LAUNCH(E, PR, SC) \
   k_count<D, E, PR, SC><<<c.grid, kThreads, 0, s>>>(DBK_COUNT_ARGS)

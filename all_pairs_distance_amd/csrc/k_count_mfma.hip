@@ -107,8 +107,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
     unsigned long long* __restrict__ counter,
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
     unsigned long long tile_cap, const int* __restrict__ perm,
-    const float* __restrict__ srow, const float* __restrict__ ncol,
-    const float* __restrict__ nexp, WalkArgs walk) {
+    const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
+    float box_thr, const float* __restrict__ srow,
+    const float* __restrict__ ncol, const float* __restrict__ nexp,
+    WalkArgs walk) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
@@ -173,6 +175,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
     // chunk of this one lands
     __syncthreads();
     stage_to_lds(srow + row0 * SR, rows_lds, kChunk4);
+    bool chunk_apart = false;
     for (int rb = 0; rb < rows; rb += 16) {
       if ((rb & 63) == 0) {
         if (rb > 0) {
@@ -189,7 +192,14 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
         if (rb + 64 < rows)
           stage_to_lds(srow + (row0 + rb + 64) * SR,
                        rows_lds + (((rb >> 6) + 1) & 1) * 64 * SR, kChunk4);
+        // pruned: these 64 rows' box provably farther than eps from this
+        // wave's columns (the barrier above is still every wave's)
+        if (PRUNED)
+          chunk_apart = wave_boxes_apart<S>(
+              boxes64 + ((row0 + rb) >> 6) * 2 * S,
+              boxes_w + (colw / (64 * P)) * 2 * S, box_thr);
       }
+      if (PRUNED && chunk_apart) continue;
       const int64_t rbase = row0 + rb;
       const float* cur = rows_lds + ((rb >> 6) & 1) * 64 * SR + (rb & 63) * SR;
       // A operand: row rbase + l16, dims of lane group q; thresholds (lo,
@@ -387,11 +397,13 @@ static hipError_t launch_count_mfma_d(const Layout& L, float eps2, bool edges,
                                       int64_t* pairs) {
   const CountPlan c = plan_count(L.n_pad, 256 * lane_points(D), pruned);
   const float* pts = pruned ? L.sorted_pts : L.pts;
+  constexpr int S = row_stride(D);
 #define DBK_MFMA_ARGS                                                        \
   pts, c.nb, c.chunks_log2, c.rows, c.items, eps2, L.count,                  \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                  \
       &L.status->n_edges, L.tiles, &L.status->n_tiles, L.tile_cap, L.perm,   \
-      L.srow, L.ncol, L.expanded ? L.nexp : nullptr, walk_args(walk, c.items)
+      L.boxes64, L.boxes_w, box_gap_threshold(eps2, S), L.srow, L.ncol,      \
+      L.expanded ? L.nexp : nullptr, walk_args(walk, c.items)
   if (edges && pruned)
     k_count_mfma<D, true, true><<<c.grid, kThreads, 0, s>>>(DBK_MFMA_ARGS);
   else if (edges)
