@@ -294,7 +294,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
   }
 }
 
-template <int D, bool EDGES, bool PRUNED, bool SCREEN>
+template <int D, bool EDGES, bool PRUNED, bool SCREEN, int PP = lane_points(D)>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_count(
     const float* __restrict__ pts, int64_t nb, int chunks_log2, int rows,
@@ -307,7 +307,7 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     float box_thr, const float* __restrict__ srow,
     const float* __restrict__ ncol, const float* __restrict__ nexp,
     WalkArgs walk) {
-  constexpr int P = lane_points(D);
+  constexpr int P = PP;
   constexpr int T = 256 * P;
   constexpr int SR = screen_stride(D);
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
@@ -356,6 +356,14 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
 
+// Small sets: with the usual P the whole triangle is a handful of tiles
+// and the pass runs on a few work-groups (64 for 2,000 points at d = 2);
+// one column point per lane gives more, shorter work items.  Measured:
+// 2k x 2 count pass 0.056 -> 0.019 ms; at 50k x 2 (5,824 items) the usual
+// P stays faster, so only launches of under 512 items switch.
+constexpr int kSmallP = 1;
+constexpr int64_t kSmallItems = 512;
+
 template <int D>
 static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
                                  bool pruned, bool screen, Walk walk,
@@ -379,6 +387,20 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
     else if (edges) DBK_LAUNCH(true, false, true);
     else if (pruned) DBK_LAUNCH(false, true, true);
     else DBK_LAUNCH(false, false, true);
+  } else if (!pruned && lane_points(D) > kSmallP && c.items < kSmallItems) {
+    const CountPlan cs = plan_count(L.n_pad, 256 * kSmallP, false);
+#define DBK_SMALL_ARGS                                                      \
+  pts, cs.nb, cs.chunks_log2, cs.rows, cs.items, eps2, L.count,             \
+      edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
+      &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
+      L.boxes_w, 0.f, L.srow, L.ncol, nullptr, walk_args(walk, cs.items)
+    if (edges)
+      k_count<D, true, false, false, kSmallP><<<cs.grid, kThreads, 0, s>>>(
+          DBK_SMALL_ARGS);
+    else
+      k_count<D, false, false, false, kSmallP><<<cs.grid, kThreads, 0, s>>>(
+          DBK_SMALL_ARGS);
+#undef DBK_SMALL_ARGS
   } else {
     if (edges && pruned) DBK_LAUNCH(true, true, false);
     else if (edges) DBK_LAUNCH(true, false, false);

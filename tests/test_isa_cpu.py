@@ -49,10 +49,12 @@ def _screened(name):
 def test_count_kernels_have_no_fused_or_packed_fp32(asm):
     bodies = kernel_bodies(asm["count"], "7k_countI")
     # 12 widths x (edges or not) x (pruned or not), exact; the 7 widths
-    # below 16 also screened (the wider ones screen on the matrix cores)
-    assert len(bodies) == 48 + 28
+    # below 16 also screened (the wider ones screen on the matrix cores);
+    # the 8 widths with several column points per lane also have the
+    # small-set kernel (one point per lane, exact, unpruned, edges or not)
+    assert len(bodies) == 48 + 28 + 16
     exact = {k: v for k, v in bodies.items() if not _screened(k)}
-    assert len(exact) == 48
+    assert len(exact) == 64
     for name, body in exact.items():
         bad = FORBIDDEN.findall(body)
         assert not bad, (name, bad[:3])
@@ -100,7 +102,7 @@ def test_tile_merge_kernels_have_no_fused_or_packed_fp32(asm):
 
 
 def test_rows_are_scalar_loads(asm):
-    bodies = kernel_bodies(asm["count"], "k_countILi3ELb0ELb0ELb0")
+    bodies = kernel_bodies(asm["count"], "k_countILi3ELb0ELb0ELb0ELi8E")
     (body,) = bodies.values()
     assert re.search(r"s_load_dword", body)
     # the distance takes its row operand straight from an SGPR
