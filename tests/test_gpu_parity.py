@@ -391,3 +391,31 @@ def test_relabel_contiguous(apd, orc):
     with pytest.raises(apd.DbscanError) as e:
         apd.relabel(bad)
     assert e.value.status == -1
+
+
+def test_random_sets_every_mode_and_walk(apd, orc):
+    """Seeded random blob sets across the compiled widths, sizes on both
+    sides of the small-set switch and of the pruning box tests, in every
+    count mode and under shuffled work orders: labels and counts must equal
+    the oracle's (the hoisted-norm mode: the oracle's hoisted-norm form)."""
+    rng = np.random.default_rng(2026)
+    for case in range(24):
+        d = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64]))
+        n = int(rng.choice([50, 700, 2000, 4097, 9000, 15000]))
+        x = datagen.gaussian_blobs(n, d, seed=int(rng.integers(1 << 30)),
+                                   n_blobs=int(rng.integers(2, 8)),
+                                   sigma=float(rng.uniform(0.01, 0.06)),
+                                   noise_frac=float(rng.uniform(0, 0.3)))
+        eps = float(rng.uniform(0.02, 0.12)) * float(np.sqrt(d))
+        m = int(rng.integers(1, 12))
+        want_l, want_c, _ = orc.fit(x, eps, m)
+        for fl, mode in ((0, "all_tiles"), (4, "pruned"), (8, "screen"),
+                         (12, "pruned_screen")):
+            for seed in (0, 5):
+                flags = fl | ((0x40 | (seed << 16)) if seed else 0)
+                lab, cnt, _ = gpu_fit(apd, x, eps, m, flags=flags)
+                assert_same(lab, cnt, want_l, want_c,
+                            f"case {case} n={n} d={d} {mode} seed={seed}")
+        want_l, want_c, _ = orc.fit(x, eps, m, form="expanded")
+        lab, cnt, _ = gpu_fit(apd, x, eps, m, flags=0x20)
+        assert_same(lab, cnt, want_l, want_c, f"case {case} n={n} d={d} expanded")
