@@ -45,13 +45,18 @@
 // When the count pass forms v on the matrix cores (v_mfma_f32_16x16x4_f32,
 // widths >= 16), the order of the additions inside an instruction, whether
 // the products are rounded on their own, the rounding mode and the
-// handling of subnormals are not specified.  The bound is then taken for
-// any order of the D additions, with every product and every sum rounded
-// off by up to 2u (any of the usual rounding modes): a product passes at
-// most D + 1 roundings, n_y at most D after its own.  So
-//   k = u + 2.01 g'_{D+1}, g'_m = 2 m u / (1 - 2 m u),
-// (the factor 2.01 covers |n_y| + sum |2 x_k y_k| <= (2+u)|y|^2 + |x|^2)
-// plus, for subnormals flushed anywhere, an absolute
+// handling of subnormals are not specified.  The products are accumulated
+// there from zero, and n_y is added last by one fp32 addition rounded to
+// nearest.  The products' sum is bounded for any order of its D - 1
+// additions, with every product and every sum rounded off by up to 2u
+// (any of the usual rounding modes), so each product passes at most D
+// roundings:
+//   |acc - sum_k P_k| <= g'_D sum |P_k| <= g'_D (|x|^2 + |y|^2),
+//   g'_m = 2 m u / (1 - 2 m u),  P_k = (-2 x_k) y_k;
+// n_y is off |y|^2 by at most u |y|^2, and the last addition by at most
+// u |n_y + acc| <= u (1 + g'_D)(|x|^2 + 2 |y|^2).  Together
+//   k = g'_D + 3u (1 + g'_D)   (taken as 1.01 g'_D + 3.01 u (1 + g'_D)),
+// plus, for subnormals flushed anywhere in the matrix unit, an absolute
 //   (2D + 2) 2^-126 (1 + 2 sqrt(Y)):
 // each product or partial sum loses at most 2^-126, and a flushed input
 // changes a product by at most 2^-126 times the other factor, itself at
@@ -129,8 +134,8 @@ __global__ __launch_bounds__(256) void k_screen_rows(
   const double u = 0x1p-24, t = 0x1p-149;
   const double gD = D * u / (1.0 - D * u);
   const double g2 = (D + 2) * u / (1.0 - (D + 2) * u);
-  const double gM = 2.0 * (D + 1) * u / (1.0 - 2.0 * (D + 1) * u);
-  const double kap = u + 2.01 * (matrix ? gM : gD);
+  const double gM = 2.0 * D * u / (1.0 - 2.0 * D * u);
+  const double kap = matrix ? 1.01 * gM + 3.01 * u * (1.0 + gM) : u + 2.01 * gD;
   // the hoisted-norm form's own error against R (see above)
   const double kapE = expanded ? u + 2.01 * gD : 0.0;
   const double e2 = (double)eps2;

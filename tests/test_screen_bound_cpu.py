@@ -10,9 +10,9 @@ is the direct fp32 distance of the rational model in pins.py.  Every pair
 the screen settles must agree with it.
 
 For the screen on the matrix cores (widths 16 and up), whose summation
-order, product rounding and rounding mode are not specified, the screen
-value is formed under several such models, each exactly, against the
-widened thresholds of that path.  With the hoisted-norm form as the
+order, product rounding and rounding mode are not specified, the products'
+sum is formed under several such models, each exactly, the norm added
+last by one rounded fp32 addition, against the thresholds of that path.  With the hoisted-norm form as the
 decision, the thresholds of that mode are checked against that form's
 exact value (pins.exact_expanded_rounded) the same way.
 """
@@ -65,8 +65,8 @@ def thresholds(x2, Y, eps2, D, kap_scale=1.0, matrix=False, expanded=False,
     u, t = 2.0 ** -24, 2.0 ** -149
     gD = D * u / (1 - D * u)
     g2 = (D + 2) * u / (1 - (D + 2) * u)
-    gM = 2 * (D + 1) * u / (1 - 2 * (D + 1) * u)
-    kap = (u + 2.01 * (gM if matrix else gD)) * kap_scale
+    gM = 2 * D * u / (1 - 2 * D * u)
+    kap = ((1.01 * gM + 3.01 * u * (1 + gM)) if matrix else (u + 2.01 * gD)) * kap_scale
     flush = (2 * D + 2) * 2.0 ** -126 * (1 + 2 * math.sqrt(Y)) * kap_scale if matrix else 0.0
     e2 = float(eps2)
     if expanded:
@@ -120,18 +120,20 @@ def round32(q, mode):
 
 
 def matrix_screen_value(x, y, D, mode, fused, order):
-    """The screen value as a matrix unit might form it: n_y plus D/4
-    instructions, instruction t adding the products of dims q*D/4 + t,
-    q = 0..3 (one per lane group).  Products exact or rounded on their own;
-    the four additions of an instruction in order, reversed, as a tree, or
-    with one rounding; every rounding in `mode`."""
+    """The screen value as the count pass forms it on a matrix unit: D/4
+    instructions accumulate from zero, instruction t adding the products
+    of dims q*D/4 + t, q = 0..3 (one per lane group), as a matrix unit
+    might: products exact or rounded on their own; the four additions of
+    an instruction in order, reversed, as a tree, or with one rounding;
+    every rounding in `mode`.  Then n_y is added by one fp32 addition
+    rounded to nearest."""
     kq = D // 4
     a = [Fraction(float(np.float32(-2.0) * v)) for v in x] + [Fraction(0)] * (D - len(x))
     b = [Fraction(float(v)) for v in y] + [Fraction(0)] * (D - len(y))
     prods = [ak * bk for ak, bk in zip(a, b)]
     if not fused:
         prods = [round32(p, mode) for p in prods]
-    acc = Fraction(float(np.float32(sq_norm64(y))))
+    acc = Fraction(0)
     for t in range(kq):
         grp = [prods[qq * kq + t] for qq in range(4)]
         if order == "seq":
@@ -146,7 +148,7 @@ def matrix_screen_value(x, y, D, mode, fused, order):
             acc = round32(acc + round32(s01 + s23, mode), mode)
         else:   # "wide": the instruction's sum rounded once
             acc = round32(acc + sum(grp), mode)
-    return acc
+    return round32(acc + Fraction(float(np.float32(sq_norm64(y)))), "rn")
 
 
 def check_pairs(pairs, eps, D, kap_scale=1.0, model=None, expanded=False,
