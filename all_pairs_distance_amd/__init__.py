@@ -20,6 +20,7 @@ _C_NAMES = {
     "FLAG_TIME_PHASES", "MAX_D",
     "MERGE_EDGES",
     "MERGE_NONE", "MERGE_TILES", "dbscan_abi_version", "dbscan_fit",
+    "dbscan_fit_counts",
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_info",
     "dbscan_status_string", "dbscan_workspace_bytes",
     "dbscan_workspace_bytes_with_edges", "dbscan_relabel_device",
@@ -40,6 +41,7 @@ def __getattr__(name):
 
 __all__ = [
     "DbscanError", "Workspace", "fit", "fit_host", "dbscan_fit",
+    "dbscan_fit_counts",
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_workspace_bytes",
     "dbscan_workspace_bytes_with_edges", "dbscan_status_string",
     "dbscan_abi_version", "dbscan_info", "relabel",
@@ -205,16 +207,21 @@ def relabel(labels, return_sizes: bool = True, stream=None):
 
 
 def fit_host(points, eps: float, min_pts: int, return_counts: bool = False):
-    """Host arrays in and out through the allocating C entry ``dbscan_fit``."""
+    """Host arrays in and out through the allocating C entries
+    ``dbscan_fit`` (labels) and ``dbscan_fit_counts`` (labels and counts)."""
     x = np.ascontiguousarray(points, dtype=np.float32)
     if x.ndim == 1:
         x = x.reshape(-1, 1)
     n, d = x.shape
     labels = np.empty(n, dtype=np.int32)
     counts = np.empty(n, dtype=np.int32) if return_counts else None
-    st = _c().dbscan_fit(x.ctypes.data if n else None, n, d, float(eps),
-                    int(min_pts), labels.ctypes.data if n else None,
-                    counts.ctypes.data if (counts is not None and n) else None)
+    if counts is None:
+        st = _c().dbscan_fit(x.ctypes.data if n else None, n, d, float(eps),
+                             int(min_pts), labels.ctypes.data if n else None)
+    else:
+        st = _c().dbscan_fit_counts(
+            x.ctypes.data if n else None, n, d, float(eps), int(min_pts),
+            labels.ctypes.data if n else None, counts.ctypes.data if n else None)
     if st != 0:
         raise DbscanError(st)
     return (labels, counts) if return_counts else labels

@@ -83,8 +83,10 @@ def _load() -> ctypes.CDLL:
                                          ctypes.c_size_t, vp, ctypes.c_uint32,
                                          ctypes.POINTER(dbscan_info)]
     lib.dbscan_fit_device_ex.restype = ctypes.c_int
-    lib.dbscan_fit.argtypes = [vp, i64, i32, f32, i32, vp, vp]
+    lib.dbscan_fit.argtypes = [vp, i64, i32, f32, i32, vp]
     lib.dbscan_fit.restype = ctypes.c_int
+    lib.dbscan_fit_counts.argtypes = [vp, i64, i32, f32, i32, vp, vp]
+    lib.dbscan_fit_counts.restype = ctypes.c_int
     lib.dbscan_relabel_workspace_bytes.argtypes = [i64]
     lib.dbscan_relabel_workspace_bytes.restype = ctypes.c_size_t
     lib.dbscan_relabel_device.argtypes = [vp, i64, vp, vp,
@@ -136,9 +138,16 @@ def dbscan_fit_device_ex(d_points: int, n: int, d: int, eps: float,
 
 
 def dbscan_fit(points: int, n: int, d: int, eps: float, min_pts: int,
-               labels: int, counts: int | None) -> int:
-    """Host-pointer entry: points/labels/counts are host addresses."""
-    return int(lib.dbscan_fit(points, n, d, eps, min_pts, labels, counts))
+               labels: int) -> int:
+    """Host-pointer entry: points/labels are host addresses."""
+    return int(lib.dbscan_fit(points, n, d, eps, min_pts, labels))
+
+
+def dbscan_fit_counts(points: int, n: int, d: int, eps: float, min_pts: int,
+                      labels: int, counts: int | None) -> int:
+    """Host-pointer entry with neighbour counts (host address or None)."""
+    return int(lib.dbscan_fit_counts(points, n, d, eps, min_pts, labels,
+                                     counts))
 
 
 def dbscan_relabel_workspace_bytes(n: int) -> int:

@@ -325,7 +325,7 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
                   : (flags & DBSCAN_FLAG_SHUFFLE_SCHEDULE) ? 2u + (flags >> 16)
                                                            : 0u};
   PhaseTimer tm((flags & DBSCAN_FLAG_TIME_PHASES) != 0, stream);
-  int64_t pass1 = 0, pass2 = 0;
+  int64_t pass1 = 0;
 
   tm.mark(0);
   DB_TRY(launch_prepare(L, d_points, stream));
@@ -337,35 +337,26 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
                       &pass1));
   tm.mark(2);
   DB_TRY(launch_core(L, min_pts, d_counts, stream));
-
+  tm.mark(3);
+  // The merge is chosen on the device from the pair count: the edge merge,
+  // then the core compaction and the tile merge, each of which exits at
+  // once when it is not the one taken.  No host round trip until the end.
+  if (want_edges) DB_TRY(launch_merge_edges(L, walk, stream));
+  DB_TRY(launch_compact(L, want_edges, stream));
+  DB_TRY(launch_merge_tiles(L, eps2, want_edges, walk, stream));
+  tm.mark(4);
+  DB_TRY(launch_label(L, d_labels, stream));
+  tm.mark(5);
+  // the one synchronisation of a fit: the status block, then the stream
   Status host_st;
   DB_TRY(hipMemcpyAsync(&host_st, L.status, sizeof(Status),
                         hipMemcpyDeviceToHost, stream));
   DB_TRY(hipStreamSynchronize(stream));
   if (host_st.nonfinite) return DBSCAN_ERR_NONFINITE;
-
   const int64_t n_core = host_st.n_core;
   const bool edges_ok = want_edges && host_st.n_edges <= L.edge_cap;
-  int mode = edges_ok ? DBSCAN_MERGE_EDGES : DBSCAN_MERGE_TILES;
-  if (!edges_ok && n_core > 0) {
-    DB_TRY(launch_compact(L, stream));
-    Status st2;
-    DB_TRY(hipMemcpyAsync(&st2, L.status, sizeof(Status),
-                          hipMemcpyDeviceToHost, stream));
-    DB_TRY(hipStreamSynchronize(stream));
-    if ((int64_t)st2.n_core_list != n_core) return DBSCAN_ERR_HIP;
-  }
-  tm.mark(3);
-  if (n_core > 0) {
-    if (edges_ok)
-      DB_TRY(launch_merge_edges(L, host_st.n_edges, walk, stream));
-    else
-      DB_TRY(launch_merge_tiles(L, eps2, n_core, walk, stream, &pass2));
-  }
-  tm.mark(4);
-  DB_TRY(launch_label(L, d_labels, stream));
-  tm.mark(5);
-  DB_TRY(hipStreamSynchronize(stream));
+  if (!edges_ok && n_core > 0 && (int64_t)host_st.n_core_list != n_core)
+    return DBSCAN_ERR_HIP;
 
   if (info) {
     info->n_core = n_core;
@@ -377,8 +368,12 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
                            ? (int64_t)host_st.n_tiles
                            : info->tiles_total;
     info->pass1_pairs = pass1;
-    info->pass2_pairs = pass2;
-    info->merge_mode = mode;
+    // the tile merge evaluates every point against the cores, padded to
+    // whole column blocks
+    const int64_t T = block_points(L.D);
+    info->pass2_pairs =
+        edges_ok ? 0 : L.n_pad * ((n_core + T - 1) / T * T);
+    info->merge_mode = edges_ok ? DBSCAN_MERGE_EDGES : DBSCAN_MERGE_TILES;
     if (tm.on) {
       info->timed = 1;
       info->ms_layout = tm.ms(0, 1);
@@ -401,8 +396,8 @@ int dbscan_fit_device(const float* d_points, int64_t n, int32_t d, float eps,
                               nullptr);
 }
 
-int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
-               int32_t min_pts, int32_t* labels, int32_t* counts) {
+int dbscan_fit_counts(const float* points, int64_t n, int32_t d, float eps,
+                      int32_t min_pts, int32_t* labels, int32_t* counts) {
   int st = check_args(n, d, eps, min_pts);
   if (st != DBSCAN_OK) return st;
   if (n > 0 && (points == nullptr || labels == nullptr))
@@ -427,11 +422,14 @@ int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
     if ((e = hipMalloc(&d_pts, pts_bytes)) != hipSuccess) break;
     if ((e = hipMalloc(&d_lab, lab_bytes)) != hipSuccess) break;
     if (counts && (e = hipMalloc(&d_cnt, lab_bytes)) != hipSuccess) break;
-    // edge area: up to a quarter of the free memory, at most 16 GiB
+    // edge area: up to a quarter of the free memory, at most 16 GiB, and
+    // no more than every pair i<j of the input could take
     size_t free_b = 0, total_b = 0;
     if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) free_b = 0;
     size_t edge_bytes = free_b / 4;
     if (edge_bytes > ((size_t)16 << 30)) edge_bytes = (size_t)16 << 30;
+    const double all_pairs = 0.5 * (double)n * (double)(n - 1) * sizeof(uint2);
+    if ((double)edge_bytes > all_pairs) edge_bytes = (size_t)all_pairs;
     ws_bytes = ws_min + align_up(edge_bytes, 256);
     if (hipMalloc(&d_ws, ws_bytes) != hipSuccess) {
       (void)hipGetLastError();
@@ -461,6 +459,11 @@ int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
   if (d_pts) (void)hipFree(d_pts);
   (void)hipStreamDestroy(stream);
   return rc;
+}
+
+int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
+               int32_t min_pts, int32_t* labels) {
+  return dbscan_fit_counts(points, n, d, eps, min_pts, labels, nullptr);
 }
 
 size_t dbscan_graph_workspace_bytes(int64_t n, int32_t d, int64_t max_pairs) {

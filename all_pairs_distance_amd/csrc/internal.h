@@ -33,6 +33,16 @@ struct Status {
 };
 static_assert(sizeof(Status) == 64, "status block is 64 bytes");
 
+// True when the fit merges by the tile pass: no edge area was offered, or
+// the count pass found more neighbour pairs than it holds.  Decided on the
+// device from the status block, so a fit needs no host round trip before
+// its merge.
+__device__ __forceinline__ bool tile_merge_needed(const Status* st,
+                                                  bool want_edges,
+                                                  unsigned long long edge_cap) {
+  return !want_edges || st->n_edges > edge_cap;
+}
+
 // Row stride of the internal point layout: d padded with zeros to the
 // compiled dimension D, then to a multiple of 4 floats (16-byte rows) when
 // D > 2 so each row is one aligned scalar/vector load.
@@ -140,11 +150,13 @@ size_t prune_sort_bytes(int64_t n_pad);
 hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s);
 hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
                        hipStream_t s);
-hipError_t launch_compact(const Layout& L, hipStream_t s);
-hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
+// The merge is chosen on the device (tile_merge_needed): the edge merge,
+// the core compaction and the tile merge are all enqueued, and the ones
+// not taken exit at once.  want_edges: an edge area was offered.
+hipError_t launch_compact(const Layout& L, bool want_edges, hipStream_t s);
+hipError_t launch_merge_edges(const Layout& L, Walk walk, hipStream_t s);
+hipError_t launch_merge_tiles(const Layout& L, float eps2, bool want_edges,
                               Walk walk, hipStream_t s);
-hipError_t launch_merge_tiles(const Layout& L, float eps2, int64_t n_core,
-                              Walk walk, hipStream_t s, int64_t* pairs);
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);
 size_t graph_sort_bytes(int64_t n);
 hipError_t launch_row_offsets(const Layout& L, const GraphLayout& G,

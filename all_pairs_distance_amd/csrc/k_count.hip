@@ -306,7 +306,7 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
     float box_thr, const float* __restrict__ srow,
     const float* __restrict__ ncol, const float* __restrict__ nexp,
-    WalkArgs walk) {
+    WalkArgs walk, const unsigned* __restrict__ nonfinite) {
   constexpr int P = PP;
   constexpr int T = 256 * P;
   constexpr int SR = screen_stride(D);
@@ -317,6 +317,8 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
   float* rows_lds = rows_all + (SCREEN ? wave * 65 * SR : 0);
   unsigned fill = 0;
   const EdgeSink sink{edges, cap, counter};
+  // a non-finite input coordinate fails the fit: skip the pass
+  if (*nonfinite) return;
   // pruned: walk the kept block pairs (written by the previous kernel);
   // if the list overflowed, every block pair of the sorted points
   bool from_list = false;
@@ -377,7 +379,7 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
       L.boxes_w, box_gap_threshold(eps2, row_stride(D)), L.srow, L.ncol,    \
       screen && L.expanded ? L.nexp : nullptr,                              \
-      walk_args(walk, c.items)
+      walk_args(walk, c.items), &L.status->nonfinite
 #define DBK_LAUNCH(E, PR, SC) \
   k_count<D, E, PR, SC><<<c.grid, kThreads, 0, s>>>(DBK_COUNT_ARGS)
   if (screen) {
@@ -393,7 +395,8 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   pts, cs.nb, cs.chunks_log2, cs.rows, cs.items, eps2, L.count,             \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
-      L.boxes_w, 0.f, L.srow, L.ncol, nullptr, walk_args(walk, cs.items)
+      L.boxes_w, 0.f, L.srow, L.ncol, nullptr, walk_args(walk, cs.items),  \
+      &L.status->nonfinite
     if (edges)
       k_count<D, true, false, false, kSmallP><<<cs.grid, kThreads, 0, s>>>(
           DBK_SMALL_ARGS);

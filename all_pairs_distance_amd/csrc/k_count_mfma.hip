@@ -110,7 +110,7 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
     const float* __restrict__ boxes64, const float* __restrict__ boxes_w,
     float box_thr, const float* __restrict__ srow,
     const float* __restrict__ ncol, const float* __restrict__ nexp,
-    WalkArgs walk) {
+    WalkArgs walk, const unsigned* __restrict__ nonfinite) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
@@ -132,6 +132,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
   uint2* stage = stage_all + (EDGES ? wave * kEdgeStage : 0);
   unsigned fill = 0;
   const EdgeSink sink{edges, cap, counter};
+  // a non-finite input coordinate fails the fit: skip the pass
+  if (*nonfinite) return;
   bool from_list = false;
   if (PRUNED) {
     const unsigned long long kept = *n_tiles;
@@ -403,7 +405,7 @@ static hipError_t launch_count_mfma_d(const Layout& L, float eps2, bool edges,
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                  \
       &L.status->n_edges, L.tiles, &L.status->n_tiles, L.tile_cap, L.perm,   \
       L.boxes64, L.boxes_w, box_gap_threshold(eps2, S), L.srow, L.ncol,      \
-      L.expanded ? L.nexp : nullptr, walk_args(walk, c.items)
+      L.expanded ? L.nexp : nullptr, walk_args(walk, c.items), &L.status->nonfinite
   if (edges && pruned)
     k_count_mfma<D, true, true><<<c.grid, kThreads, 0, s>>>(DBK_MFMA_ARGS);
   else if (edges)

@@ -26,16 +26,23 @@
 
 namespace dbk {
 
+// Grid-stride over the recorded pairs; their number is read from the
+// status block (the host never waits for it).  Exits at once when the
+// pairs overflowed the edge area (the tile merge runs instead) or there is
+// no core point.
 __global__ void k_merge_edges(const uint2* __restrict__ edges,
-                              unsigned long long ne,
+                              unsigned long long edge_cap,
                               const unsigned char* __restrict__ core,
                               int* parent, int* __restrict__ bmin,
-                              WalkArgs walk) {
+                              const Status* __restrict__ st, WalkArgs walk) {
+  const unsigned long long ne = st->n_edges;
+  if (ne > edge_cap || st->n_core == 0) return;
+  // (a test mode walks the pairs in another order: results must not
+  // change)
+  walk_refit((int64_t)ne, walk.mul, walk.add);
   for (unsigned long long k = blockIdx.x * (unsigned long long)blockDim.x +
                               threadIdx.x;
        k < ne; k += (unsigned long long)gridDim.x * blockDim.x) {
-    // (a test mode walks the pairs in another order: results must not
-    // change)
     const unsigned long long e =
         (unsigned long long)walk_item((int64_t)k, (int64_t)ne, walk.mul, walk.add);
     const uint2 ij = edges[e];
@@ -50,14 +57,17 @@ __global__ void k_merge_edges(const uint2* __restrict__ edges,
   }
 }
 
-hipError_t launch_merge_edges(const Layout& L, unsigned long long n_edges,
-                              Walk walk, hipStream_t s) {
-  if (n_edges == 0) return hipSuccess;
-  unsigned long long g = (n_edges + 255) / 256;
-  if (g > (unsigned long long)kMaxGrid) g = kMaxGrid;
-  k_merge_edges<<<(unsigned)g, 256, 0, s>>>(L.edges, n_edges, L.core,
-                                            L.parent, L.bmin,
-                                            walk_args(walk, (int64_t)n_edges));
+// Enough work-groups to fill every CU at full occupancy (256 CUs x 8 of
+// 256 threads); the pair count is only known on the device.
+constexpr unsigned kMergeGrid = 2048;
+
+hipError_t launch_merge_edges(const Layout& L, Walk walk, hipStream_t s) {
+  if (L.edge_cap == 0) return hipSuccess;
+  unsigned long long g = (L.edge_cap + 255) / 256;
+  if (g > kMergeGrid) g = kMergeGrid;
+  k_merge_edges<<<(unsigned)g, 256, 0, s>>>(
+      L.edges, L.edge_cap, L.core, L.parent, L.bmin, L.status,
+      walk_args(walk, (int64_t)(L.edge_cap < 2 ? 2 : L.edge_cap)));
   return hipGetLastError();
 }
 
@@ -65,22 +75,31 @@ typedef const unsigned char __attribute__((address_space(4)))* const_u8_ptr;
 
 // EXPANDED: pairs are decided with the hoisted-norm form, from the norm
 // table nexp (indexed by original point).
+// Work items are (1024-row block) x (T-core column block) pairs, walked
+// grid-stride; the number of column blocks follows from the core count,
+// read on the device.  Exits at once unless the fit merges by tiles.
 template <int D, bool EXPANDED>
 __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     const float* __restrict__ pts, const float* __restrict__ core_pts,
     const int* __restrict__ core_list, const unsigned char* __restrict__ core,
-    int64_t row_blocks, int64_t col_blocks, float eps2, int* parent,
-    int* __restrict__ bmin, const float* __restrict__ nexp, int64_t n_core,
-    WalkArgs walk_r, WalkArgs walk_c) {
+    int64_t row_blocks, float eps2, int* parent, int* __restrict__ bmin,
+    const float* __restrict__ nexp, const Status* __restrict__ st,
+    bool want_edges, unsigned long long edge_cap, WalkArgs walk_r,
+    WalkArgs walk_c) {
   constexpr int P = lane_points(D);
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
+  const int64_t n_core = st->n_core_list;
+  if (n_core == 0 || !tile_merge_needed(st, want_edges, edge_cap)) return;
+  const int64_t col_blocks = (n_core + T - 1) / T;
+  const int64_t items = row_blocks * col_blocks;
+  walk_refit(col_blocks, walk_c.mul, walk_c.add);
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  for (int64_t rs = blockIdx.y; rs < row_blocks; rs += gridDim.y)
-  for (int64_t cs = blockIdx.x; cs < col_blocks; cs += gridDim.x) {
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     // (a test mode walks the blocks in another order: results must not
     // change)
+    const int64_t rs = item / col_blocks, cs = item - rs * col_blocks;
     const int64_t rblk = walk_item(rs, row_blocks, walk_r.mul, walk_r.add);
     const int64_t cblk = walk_item(cs, col_blocks, walk_c.mul, walk_c.add);
     const int64_t row0 = rblk * kRowsPerItem;
@@ -90,13 +109,15 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     float pc[EXPANDED ? P : 1];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
+      // columns past the cores are NaN (never a neighbour); their list
+      // entries and coordinates were not written and are not read
       const int64_t c = colw + p * 64 + lane;
-      cidx[p] = core_list[c];
+      const bool real = c < n_core;
+      cidx[p] = real ? core_list[c] : INT_MAX;
 #pragma unroll
-      for (int k = 0; k < D; ++k) xc[p][k] = core_pts[c * S + k];
-      // columns past the cores have NaN coordinates and never match (their
-      // core_list entries are not written): no norm is read for them
-      if (EXPANDED) pc[p] = c < n_core ? nexp[cidx[p]] : 0.f;
+      for (int k = 0; k < D; ++k)
+        xc[p][k] = real ? core_pts[c * S + k] : __builtin_nanf("");
+      if (EXPANDED) pc[p] = real ? nexp[cidx[p]] : 0.f;
     }
     for (int rb = 0; rb < kRowsPerItem; rb += 64) {
       int rowmin = INT_MAX;  // lane l: lowest core neighbour of row rb+l
@@ -132,44 +153,35 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
 
 template <int D>
 static hipError_t launch_merge_tiles_d(const Layout& L, float eps2,
-                                       int64_t n_core, Walk walk,
-                                       hipStream_t s, int64_t* pairs) {
+                                       bool want_edges, Walk walk,
+                                       hipStream_t s) {
   constexpr int T = 256 * lane_points(D);
-  const int64_t nc_pad = (n_core + T - 1) / T * T;
-  const int64_t col_blocks = nc_pad / T;
   const int64_t row_blocks = L.n_pad / kRowsPerItem;
-  if (row_blocks == 0 || col_blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)(col_blocks < 4096 ? col_blocks : 4096),
-                  (unsigned)(row_blocks < 4096 ? row_blocks : 4096));
+  // sized for the most items (every point a core); the excess exits
+  const int64_t most = row_blocks * (L.n_pad / T);
+  const unsigned grid = (unsigned)(most < 4096 ? most : 4096);
+  const WalkArgs wr = walk_args(walk, row_blocks);
+  const WalkArgs wc = walk_args(walk, L.n_pad / T < 2 ? 2 : L.n_pad / T);
   if (L.expanded)
     k_merge_tiles<D, true><<<grid, kThreads, 0, s>>>(
-        L.pts, L.core_pts, L.core_list, L.core, row_blocks, col_blocks, eps2,
-        L.parent, L.bmin, L.nexp, n_core, walk_args(walk, row_blocks),
-        walk_args(walk, col_blocks));
+        L.pts, L.core_pts, L.core_list, L.core, row_blocks, eps2, L.parent,
+        L.bmin, L.nexp, L.status, want_edges, L.edge_cap, wr, wc);
   else
     k_merge_tiles<D, false><<<grid, kThreads, 0, s>>>(
-        L.pts, L.core_pts, L.core_list, L.core, row_blocks, col_blocks, eps2,
-        L.parent, L.bmin, nullptr, n_core, walk_args(walk, row_blocks),
-        walk_args(walk, col_blocks));
-  if (pairs) *pairs = L.n_pad * nc_pad;
+        L.pts, L.core_pts, L.core_list, L.core, row_blocks, eps2, L.parent,
+        L.bmin, nullptr, L.status, want_edges, L.edge_cap, wr, wc);
   return hipGetLastError();
 }
 
-hipError_t launch_merge_tiles(const Layout& L, float eps2, int64_t n_core,
-                              Walk walk, hipStream_t s, int64_t* pairs) {
+hipError_t launch_merge_tiles(const Layout& L, float eps2, bool want_edges,
+                              Walk walk, hipStream_t s) {
   switch (L.D) {
-    case 1: return launch_merge_tiles_d<1>(L, eps2, n_core, walk, s, pairs);
-    case 2: return launch_merge_tiles_d<2>(L, eps2, n_core, walk, s, pairs);
-    case 3: return launch_merge_tiles_d<3>(L, eps2, n_core, walk, s, pairs);
-    case 4: return launch_merge_tiles_d<4>(L, eps2, n_core, walk, s, pairs);
-    case 6: return launch_merge_tiles_d<6>(L, eps2, n_core, walk, s, pairs);
-    case 8: return launch_merge_tiles_d<8>(L, eps2, n_core, walk, s, pairs);
-    case 12: return launch_merge_tiles_d<12>(L, eps2, n_core, walk, s, pairs);
-    case 16: return launch_merge_tiles_d<16>(L, eps2, n_core, walk, s, pairs);
-    case 24: return launch_merge_tiles_d<24>(L, eps2, n_core, walk, s, pairs);
-    case 32: return launch_merge_tiles_d<32>(L, eps2, n_core, walk, s, pairs);
-    case 48: return launch_merge_tiles_d<48>(L, eps2, n_core, walk, s, pairs);
-    case 64: return launch_merge_tiles_d<64>(L, eps2, n_core, walk, s, pairs);
+#define DBK_CASE(DD) \
+  case DD: return launch_merge_tiles_d<DD>(L, eps2, want_edges, walk, s);
+    DBK_CASE(1) DBK_CASE(2) DBK_CASE(3) DBK_CASE(4) DBK_CASE(6) DBK_CASE(8)
+    DBK_CASE(12) DBK_CASE(16) DBK_CASE(24) DBK_CASE(32) DBK_CASE(48)
+    DBK_CASE(64)
+#undef DBK_CASE
     default: return hipErrorInvalidValue;
   }
 }

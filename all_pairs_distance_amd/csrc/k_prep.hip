@@ -67,49 +67,46 @@ hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s) {
 }
 
 // core[i] = count[i] >= min_pts (Wang et al., Sec. II item 2: at least
-// MinPts points within eps); copies the counts out if asked.
-__global__ void k_core(const unsigned* __restrict__ count, int64_t n,
-                       int64_t n_pad, int min_pts,
-                       unsigned char* __restrict__ core,
-                       int* __restrict__ counts_out, Status* __restrict__ st) {
-  unsigned mine = 0;
-  // n_pad is a multiple of the block size, so whole waves enter together
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const unsigned c = count[i];
-    const bool is_core = i < n && c >= (unsigned)min_pts;
-    core[i] = is_core ? 1 : 0;
-    if (counts_out && i < n) counts_out[i] = (int)c;
-    mine += (unsigned)__popcll(ballot(is_core));
-  }
-  if (lane_id() == 0 && mine) atomicAdd(&st->n_core, mine);
-}
-
-hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
-                       hipStream_t s) {
-  k_core<<<grid_for(L.n_pad, 256 * 4), 256, 0, s>>>(
-      L.count, L.n, L.n_pad, min_pts, L.core, counts_out, L.status);
-  return hipGetLastError();
-}
-
-// ---- sorted compaction of the core points (tile merge only) --------------
-// Blocks of 1024 points: per-block core totals, one exclusive scan over
-// the totals, then each block writes its cores in index order.
-
-__global__ __launch_bounds__(256) void k_core_block_totals(
-    const unsigned char* __restrict__ core, int64_t n_pad,
-    unsigned* __restrict__ sums) {
+// MinPts points within eps); copies the counts out if asked.  Each
+// workgroup takes 1024 consecutive points, four per thread (one 16-byte
+// load of counts, one 4-byte store of flags), and writes the number of
+// core points among them to sums[block]: no atomics (one same-address
+// atomic per wave serialised this pass at 1M points).  k_scan_totals then
+// turns the totals into offsets and the core count.  n_pad is a multiple
+// of 1024, so every workgroup is full.
+__global__ __launch_bounds__(256) void k_core(
+    const unsigned* __restrict__ count, int64_t n, int min_pts,
+    unsigned char* __restrict__ core, int* __restrict__ counts_out,
+    bool out_vec, unsigned* __restrict__ sums) {
   __shared__ unsigned sh[4];
   const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
-  unsigned c = 0;
-  if (base < n_pad)
-    c = core[base] + core[base + 1] + core[base + 2] + core[base + 3];
+  const uint4 c4 = *reinterpret_cast<const uint4*>(count + base);
+  const unsigned c[4] = {c4.x, c4.y, c4.z, c4.w};
+  unsigned flags = 0, mine = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned is_core = base + q < n && c[q] >= (unsigned)min_pts;
+    flags |= is_core << (8 * q);
+    mine += is_core;
+  }
+  *reinterpret_cast<unsigned*>(core + base) = flags;
+  if (counts_out != nullptr) {
+    if (out_vec && base + 4 <= n) {
+      *reinterpret_cast<int4*>(counts_out + base) =
+          make_int4((int)c[0], (int)c[1], (int)c[2], (int)c[3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (base + q < n) counts_out[base + q] = (int)c[q];
+    }
+  }
   unsigned tot;
-  block_excl_scan(c, sh, &tot);
+  block_excl_scan(mine, sh, &tot);
   if (threadIdx.x == 0) sums[blockIdx.x] = tot;
 }
 
-// Exclusive scan of the block totals in place, by one workgroup.
+// Exclusive scan of the per-block core totals in place, by one workgroup;
+// the total is the number of core points.
 __global__ __launch_bounds__(256) void k_scan_totals(unsigned* sums,
                                                      int64_t nblk,
                                                      Status* st) {
@@ -123,18 +120,38 @@ __global__ __launch_bounds__(256) void k_scan_totals(unsigned* sums,
     if (b < nblk) sums[b] = carry + ex;
     carry += tot;
   }
-  if (threadIdx.x == 0) st->n_core_list = carry;
+  if (threadIdx.x == 0) {
+    st->n_core = carry;
+    st->n_core_list = carry;
+  }
 }
 
+hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
+                       hipStream_t s) {
+  const int64_t nblk = L.n_pad / 1024;
+  const bool out_vec = ((uintptr_t)counts_out & 15u) == 0;
+  k_core<<<(unsigned)nblk, 256, 0, s>>>(L.count, L.n, min_pts, L.core,
+                                        counts_out, out_vec, L.block_sums);
+  k_scan_totals<<<1, 256, 0, s>>>(L.block_sums, nblk, L.status);
+  return hipGetLastError();
+}
+
+// ---- sorted compaction of the core points (tile merge only) --------------
+// Each block of 1024 points writes its cores in index order at the offset
+// k_scan_totals gave it.  Launched on every fit that may need it; exits at
+// once when the edge merge runs or there is no core point.
 __global__ __launch_bounds__(256) void k_core_scatter(
     const unsigned char* __restrict__ core, const float* __restrict__ pts,
-    int64_t n_pad, int S, const unsigned* __restrict__ sums,
-    int* __restrict__ core_list, float* __restrict__ core_pts) {
+    int S, const unsigned* __restrict__ sums, int* __restrict__ core_list,
+    float* __restrict__ core_pts, const Status* __restrict__ st,
+    bool want_edges, unsigned long long edge_cap) {
+  if (st->n_core == 0 || !tile_merge_needed(st, want_edges, edge_cap)) return;
   __shared__ unsigned sh[4];
   const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
-  unsigned f[4] = {0, 0, 0, 0};
-  if (base < n_pad)
-    for (int q = 0; q < 4; ++q) f[q] = core[base + q];
+  const unsigned f4 = *reinterpret_cast<const unsigned*>(core + base);
+  unsigned f[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) f[q] = (f4 >> (8 * q)) & 0xffu;
   unsigned tot;
   unsigned pos = sums[blockIdx.x] +
                  block_excl_scan(f[0] + f[1] + f[2] + f[3], sh, &tot);
@@ -148,22 +165,11 @@ __global__ __launch_bounds__(256) void k_core_scatter(
   }
 }
 
-__global__ void k_fill_nan(float* __restrict__ p, int64_t total) {
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x)
-    p[e] = __builtin_nanf("");
-}
-
-hipError_t launch_compact(const Layout& L, hipStream_t s) {
+hipError_t launch_compact(const Layout& L, bool want_edges, hipStream_t s) {
   const int64_t nblk = L.n_pad / 1024;
-  k_fill_nan<<<grid_for(L.n_pad * L.stride, 256 * 8), 256, 0, s>>>(
-      L.core_pts, L.n_pad * L.stride);
-  k_core_block_totals<<<(unsigned)nblk, 256, 0, s>>>(L.core, L.n_pad,
-                                                      L.block_sums);
-  k_scan_totals<<<1, 256, 0, s>>>(L.block_sums, nblk, L.status);
   k_core_scatter<<<(unsigned)nblk, 256, 0, s>>>(
-      L.core, L.pts, L.n_pad, L.stride, L.block_sums, L.core_list,
-      L.core_pts);
+      L.core, L.pts, L.stride, L.block_sums, L.core_list, L.core_pts,
+      L.status, want_edges, L.edge_cap);
   return hipGetLastError();
 }
 

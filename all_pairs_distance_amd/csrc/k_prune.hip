@@ -193,25 +193,39 @@ __device__ __forceinline__ void key_coords(const float* __restrict__ p, int KD,
 }
 
 // Global min/max of the first KD coordinates of the real points
-// (lohi: KD minima, then KD maxima, order-encoded).
-__global__ void k_bbox(const float* __restrict__ pts, int64_t n, int S, int KD,
-                       int d, const float* __restrict__ pca,
-                       unsigned* __restrict__ lohi) {
+// (lohi: KD minima, then KD maxima, order-encoded).  Reduced per wave with
+// shuffles, then per workgroup in LDS, so each workgroup issues one atomic
+// per bound: one per wave on these 2*KD words serialised the pass.
+__global__ __launch_bounds__(256) void k_bbox(
+    const float* __restrict__ pts, int64_t n, int S, int KD, int d,
+    const float* __restrict__ pca, unsigned* __restrict__ lohi) {
+  __shared__ unsigned sh[4][2 * kKeyDims];
   unsigned lo[kKeyDims], hi[kKeyDims];
   for (int k = 0; k < kKeyDims; ++k) {
     lo[k] = ~0u;
     hi[k] = 0u;
   }
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    float y[kKeyDims], r2;
-    key_coords(pts + i * S, KD, d, S, pca, y, &r2);
-    for (int k = 0; k < KD; ++k) {
-      const unsigned u = ord_u(y[k]);
-      lo[k] = u < lo[k] ? u : lo[k];
-      hi[k] = u > hi[k] ? u : hi[k];
+  // four points per thread and step, their loads issued together
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i0 < n;
+       i0 += 4 * stride) {
+    float y[4][kKeyDims], r2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n) key_coords(pts + i * S, KD, d, S, pca, y[u], &r2);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u * stride >= n) break;
+      for (int k = 0; k < KD; ++k) {
+        const unsigned v = ord_u(y[u][k]);
+        lo[k] = v < lo[k] ? v : lo[k];
+        hi[k] = v > hi[k] ? v : hi[k];
+      }
     }
   }
+  const int wave = threadIdx.x >> 6;
   for (int k = 0; k < KD; ++k) {
     unsigned a = lo[k], b = hi[k];
     for (int off = 32; off > 0; off >>= 1) {
@@ -220,9 +234,20 @@ __global__ void k_bbox(const float* __restrict__ pts, int64_t n, int S, int KD,
       b = ob > b ? ob : b;
     }
     if (lane_id() == 0) {
-      atomicMin(lohi + k, a);
-      atomicMax(lohi + KD + k, b);
+      sh[wave][k] = a;
+      sh[wave][KD + k] = b;
     }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 2 * KD) {
+    unsigned v = sh[0][t];
+    for (int w = 1; w < 4; ++w) {
+      const unsigned o = sh[w][t];
+      v = t < KD ? (o < v ? o : v) : (o > v ? o : v);
+    }
+    if (t < KD) atomicMin(lohi + t, v);
+    else atomicMax(lohi + t, v);
   }
 }
 
@@ -409,8 +434,11 @@ hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s) {
   const float* pca = wide ? L.pca : nullptr;
   if (wide) k_pca<<<1, 256, 0, s>>>(L.pts, L.n, L.stride, L.d, L.pca);
   k_bbox_init<<<1, 64, 0, s>>>(L.bbox, KD);
-  k_bbox<<<grid_for_p(L.n, 256 * 16), 256, 0, s>>>(L.pts, L.n, L.stride, KD,
-                                                   L.d, pca, L.bbox);
+  // at most 512 work-groups (one atomic per bound each), 4+ points per
+  // thread
+  const unsigned bgrid = grid_for_p(L.n, 256 * 4);
+  k_bbox<<<bgrid < 512 ? bgrid : 512, 256, 0, s>>>(L.pts, L.n, L.stride, KD,
+                                                     L.d, pca, L.bbox);
   k_keys<<<grid_for_p(L.n_pad, 256 * 4), 256, 0, s>>>(
       L.pts, L.n, L.n_pad, L.stride, KD, L.d, pca, L.bbox, L.keys_in,
       L.idx_in);

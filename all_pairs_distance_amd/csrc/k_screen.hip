@@ -95,31 +95,52 @@ __device__ __forceinline__ float sq_norm32(const float* __restrict__ p, int S) {
 }
 
 // Pass 1: fp32 norms of every point and the largest fp64 squared norm
-// (and, for the hoisted-norm form, its own fp32 norm of every point).
+// (and, for the hoisted-norm form, its own fp32 norm of every point).  The
+// maximum is reduced per wave, then per workgroup in LDS: one atomic per
+// workgroup (one per wave on the same word serialised the pass).
 __global__ __launch_bounds__(256) void k_screen_norms(
     const float* __restrict__ pts, int64_t n_pad, int S,
     float* __restrict__ ncol, float* __restrict__ nexp,
     Status* __restrict__ st) {
+  __shared__ double sh[4];
   double ymax = 0.0;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const double s = sq_norm64(pts + i * S, S);
-    if (s == s) {                    // real point (padding rows are NaN)
-      ncol[i] = (float)s;            // round to nearest
-      ymax = s > ymax ? s : ymax;
-    } else {
-      ncol[i] = __builtin_nanf("");
+  // four points per thread and step, their loads issued together
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+       i0 < n_pad; i0 += 4 * stride) {
+    double s[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      s[u] = i < n_pad ? sq_norm64(pts + i * S, S) : 0.0;
     }
-    if (nexp) nexp[i] = sq_norm32(pts + i * S, S);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i >= n_pad) break;
+      if (s[u] == s[u]) {              // real point (padding rows are NaN)
+        ncol[i] = (float)s[u];         // round to nearest
+        ymax = s[u] > ymax ? s[u] : ymax;
+      } else {
+        ncol[i] = __builtin_nanf("");
+      }
+      if (nexp) nexp[i] = sq_norm32(pts + i * S, S);
+    }
   }
   for (int off = 32; off > 0; off >>= 1) {
     const double o = __shfl_xor(ymax, off);
     ymax = o > ymax ? o : ymax;
   }
-  if (lane_id() == 0 && ymax > 0.0) {
-    // non-negative doubles order like their bit patterns
-    atomicMax(&st->ymax_bits, (unsigned long long)__double_as_longlong(ymax));
-    if (!(ymax <= 0x1p100)) atomicOr(&st->screen_unsafe, 1u);
+  if (lane_id() == 0) sh[threadIdx.x >> 6] = ymax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ymax = sh[0];
+    for (int w = 1; w < 4; ++w) ymax = sh[w] > ymax ? sh[w] : ymax;
+    if (ymax > 0.0) {
+      // non-negative doubles order like their bit patterns
+      atomicMax(&st->ymax_bits, (unsigned long long)__double_as_longlong(ymax));
+      if (!(ymax <= 0x1p100)) atomicOr(&st->screen_unsafe, 1u);
+    }
   }
 }
 
@@ -184,7 +205,9 @@ __global__ __launch_bounds__(256) void k_screen_rows(
 
 hipError_t launch_screen(const Layout& L, const float* pts, float eps2,
                          hipStream_t s) {
-  k_screen_norms<<<grid_for_s(L.n_pad, 256 * 4), 256, 0, s>>>(
+  // at most 512 work-groups: one atomic each
+  const unsigned ngrid = grid_for_s(L.n_pad, 256 * 4);
+  k_screen_norms<<<ngrid < 512 ? ngrid : 512, 256, 0, s>>>(
       pts, L.n_pad, L.stride, L.ncol, L.expanded ? L.nexp : nullptr,
       L.status);
   const unsigned grid = grid_for_s(L.n_pad, 256 * 4);

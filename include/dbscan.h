@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DBSCAN_ABI_VERSION 1
+#define DBSCAN_ABI_VERSION 2
 #define DBSCAN_MAX_D 64
 
 /* Status codes: 0 on success, negative on failure.  On any failure the
@@ -51,7 +51,8 @@ typedef enum dbscan_status {
   DBSCAN_ERR_NONFINITE = -2,   /* a coordinate is NaN or +-inf */
   DBSCAN_ERR_NO_DEVICE = -3,   /* no HIP device, or the current device is
                                   not gfx950 */
-  DBSCAN_ERR_OOM = -4,         /* dbscan_fit only: device allocation failed */
+  DBSCAN_ERR_OOM = -4,         /* dbscan_fit and dbscan_fit_counts only:
+                                  device allocation failed */
   DBSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than
                                   dbscan_workspace_bytes(n, d), or misaligned */
   DBSCAN_ERR_HIP = -6,         /* any other HIP runtime error */
@@ -172,12 +173,14 @@ size_t dbscan_workspace_bytes_with_edges(int64_t n, int32_t d,
  *              when every neighbour pair fits there the merge reuses them,
  *              otherwise it re-evaluates distances (same result, slower).
  *   hip_stream hipStream_t passed as void*; NULL = the default stream.
- * All kernels run on hip_stream.  The call synchronises that stream
- * (twice: once to size the merge, once at the end) so the returned status
- * is final; it is not capturable into a HIP graph.  Calls on different
- * streams with different workspaces may run concurrently; two calls must
- * not share a workspace at the same time.  The library keeps no state
- * between calls. */
+ * All kernels run on hip_stream.  The call synchronises that stream once,
+ * after the last kernel, so the returned status is final (the choice
+ * between the edge merge and the tile merge is taken on the device).  It
+ * is not capturable into a HIP graph (that synchronisation, and a
+ * device-to-host copy of a 64-byte status block into host memory).  Calls
+ * on different streams with different workspaces may run concurrently; two
+ * calls must not share a workspace at the same time.  The library keeps no
+ * state between calls. */
 int dbscan_fit_device(const float* d_points, int64_t n, int32_t d, float eps,
                       int32_t min_pts, int32_t* d_labels, int32_t* d_counts,
                       void* d_workspace, size_t workspace_bytes,
@@ -194,10 +197,20 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
 /* Fit from host memory: allocates device memory (points, labels, counts,
  * workspace with an edge area sized from free device memory), copies in,
  * fits on a stream of its own, copies out and frees everything before
- * returning.  labels: host, n int32.  counts: host, n int32, or NULL.
- * Blocking. */
+ * returning.  Blocking.
+ *   points  host, n*d fp32, row-major; read only; caller-owned.
+ *   labels  host, n int32; written; caller-owned.
+ * The problem is the one Wang et al. Sec. II states (points, eps and MinPts
+ * in; clusters and noise out); the arguments are those of the contract
+ * dbscan_fit(points[N x d], N, d, eps, minPts) -> labels. */
 int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
-               int32_t min_pts, int32_t* labels, int32_t* counts);
+               int32_t min_pts, int32_t* labels);
+
+/* As dbscan_fit, and also copies out the neighbour counts (self included):
+ * counts is host, n int32, caller-owned, or NULL (then exactly
+ * dbscan_fit). */
+int dbscan_fit_counts(const float* points, int64_t n, int32_t d, float eps,
+                      int32_t min_pts, int32_t* labels, int32_t* counts);
 
 /* Contiguous cluster ids from the labels of a fit: clusters are numbered
  * 0..K-1 in ascending order of their label (their smallest member, so the

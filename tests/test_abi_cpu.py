@@ -18,9 +18,79 @@ def declared_functions():
     return sorted(set(names))
 
 
+def prototypes():
+    """{name: (return type, [parameter types])} of every function the header
+    declares, with parameter names and comments dropped."""
+    text = open(_capi.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)
+    out = {}
+    for ret, name, params in re.findall(
+            r"((?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**)\s*\b(dbscan_[a-z_]+)\s*"
+            r"\(([^()]*)\)\s*;", text):
+        types = []
+        for p in params.split(","):
+            p = " ".join(p.split())
+            if p in ("", "void"):
+                continue
+            # drop the parameter name: the last identifier
+            m = re.match(r"(.*?[\s*])([A-Za-z_][A-Za-z0-9_]*)$", p)
+            types.append(m.group(1).replace(" *", "*").strip())
+        out[name] = (" ".join(ret.split()).replace(" *", "*"), types)
+    return out
+
+
+# The boundary's entry points with their exact signatures (return type and
+# parameter types in order): dbscan_fit(points[N x d] fp32, N, d, eps,
+# minPts) -> int32 labels, the device-pointer form with its caller-owned
+# workspace and stream, the workspace query, the status strings and the ABI
+# version.
+CONTRACT = {
+    "dbscan_fit": ("int", ["const float*", "int64_t", "int32_t", "float",
+                           "int32_t", "int32_t*"]),
+    "dbscan_fit_device": ("int", ["const float*", "int64_t", "int32_t",
+                                  "float", "int32_t", "int32_t*", "int32_t*",
+                                  "void*", "size_t", "void*"]),
+    "dbscan_workspace_bytes": ("size_t", ["int64_t", "int32_t"]),
+    "dbscan_status_string": ("const char*", ["int"]),
+    "dbscan_abi_version": ("int", []),
+}
+
+
+def test_header_prototypes_match_the_contract():
+    protos = prototypes()
+    for name, want in CONTRACT.items():
+        assert protos.get(name) == want, (name, protos.get(name))
+    # every declared function was parsed
+    assert set(protos) == set(declared_functions())
+    text = open(_capi.HEADER_PATH).read()
+    codes = dict((k, int(v)) for k, v in
+                 re.findall(r"(DBSCAN_ERR_[A-Z_]+|DBSCAN_OK) = (-?\d+)", text))
+    for name, value in (("DBSCAN_OK", 0), ("DBSCAN_ERR_INVALID_ARG", -1),
+                        ("DBSCAN_ERR_NONFINITE", -2), ("DBSCAN_ERR_NO_DEVICE", -3),
+                        ("DBSCAN_ERR_OOM", -4), ("DBSCAN_ERR_WORKSPACE", -5),
+                        ("DBSCAN_ERR_HIP", -6)):
+        assert codes[name] == value
+
+
+def test_binding_arity_matches_the_header():
+    lib = _capi.lib
+    for name, (_, types) in prototypes().items():
+        assert len(getattr(lib, name).argtypes) == len(types), name
+
+
+def test_readme_calls_the_contract_signature():
+    import os
+    readme = open(os.path.join(os.path.dirname(_capi.HEADER_PATH), "..",
+                               "README.md")).read()
+    for call in re.findall(r"\bdbscan_fit\(([^;]*)\);", readme):
+        assert len(call.split(",")) == 6, call
+
+
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("dbscan_fit", "dbscan_fit_device", "dbscan_fit_device_ex",
+    for want in ("dbscan_fit", "dbscan_fit_counts", "dbscan_fit_device",
+                 "dbscan_fit_device_ex",
                  "dbscan_workspace_bytes", "dbscan_workspace_bytes_with_edges",
                  "dbscan_status_string", "dbscan_abi_version",
                  "dbscan_relabel_device", "dbscan_relabel_workspace_bytes",
@@ -124,7 +194,15 @@ def test_graph_invalid_arguments_rejected_before_device_work():
 def _status(points, n, d, eps, m, labels=True):
     lab = np.empty(max(n, 1), np.int32)
     return apd.dbscan_fit(points.ctypes.data if points is not None else None,
-                          n, d, eps, m, lab.ctypes.data if labels else None, None)
+                          n, d, eps, m, lab.ctypes.data if labels else None)
+
+
+def _status_counts(points, n, d, eps, m, labels=True):
+    lab = np.empty(max(n, 1), np.int32)
+    cnt = np.empty(max(n, 1), np.int32)
+    return apd.dbscan_fit_counts(
+        points.ctypes.data if points is not None else None, n, d, eps, m,
+        lab.ctypes.data if labels else None, cnt.ctypes.data)
 
 
 def test_invalid_arguments_rejected_before_device_work():
@@ -140,6 +218,10 @@ def test_invalid_arguments_rejected_before_device_work():
     assert _status(None, 8, 2, 0.1, 1) == _capi.ERR_INVALID_ARG
     assert _status(x, 8, 2, 0.1, 1, labels=False) == _capi.ERR_INVALID_ARG
     assert _status(None, 0, 2, 0.1, 1, labels=False) == _capi.OK
+    assert _status_counts(x, 8, 2, 0.1, 0) == _capi.ERR_INVALID_ARG
+    assert _status_counts(x, 8, 2, float("nan"), 1) == _capi.ERR_INVALID_ARG
+    assert _status_counts(x, 8, 2, 0.1, 1, labels=False) == _capi.ERR_INVALID_ARG
+    assert _status_counts(None, 0, 2, 0.1, 1, labels=False) == _capi.OK
     ws = np.zeros(16, np.uint8)
     st = apd.dbscan_fit_device_ex(x.ctypes.data, 8, 2, 0.1, 1, ws.ctypes.data,
                                   None, ws.ctypes.data, 16, None, 0x80, None)

@@ -260,11 +260,15 @@ def test_named_workload(apd, orc, key, flags, mode):
     print(f"workload {key} {w.name} {mode}", flush=True)
     lab, cnt, info = gpu_fit(apd, x, eps, m, max_edges=1 << 30, flags=flags)
     assert info["merge_mode"] == 1
+    # full-size parity: every count and every label against the oracle's
+    # stored digests, for exactly these input bytes (no fallback)
     g = _golden().get(str(key))
-    if g is not None and g["points_sha256"] == datagen.sha256_points(x):
-        assert _digest(cnt) == g["counts_sha256"], "counts differ from the oracle"
-        assert _digest(lab) == g["labels_sha256"], "labels differ from the oracle"
-        assert int(info["n_core"]) == g["n_core"]
+    assert g is not None, f"no oracle digests stored for workload {key}"
+    assert g["points_sha256"] == datagen.sha256_points(x), \
+        "the generator's output changed since the oracle digests were written"
+    assert _digest(cnt) == g["counts_sha256"], "counts differ from the oracle"
+    assert _digest(lab) == g["labels_sha256"], "labels differ from the oracle"
+    assert int(info["n_core"]) == g["n_core"]
     # rows recomputed by the oracle right now
     rng = np.random.default_rng(key)
     rows = rng.choice(w.n, size=min(w.n, 192), replace=False)

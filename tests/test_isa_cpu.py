@@ -23,7 +23,9 @@ def kernel_bodies(asm: str, marker: str):
     out = {}
     for m in re.finditer(r"^(_Z\S*" + marker + r"\S*):", asm, flags=re.M):
         name = m.group(1)
-        end = asm.find("s_endpgm", m.end())
+        # the whole function: a kernel may end in several places (early
+        # exits), so read to the assembler's end-of-function label
+        end = asm.find(".Lfunc_end", m.end())
         out[name] = asm[m.end():end]
     return out
 
