@@ -20,7 +20,8 @@ _C_NAMES = {
     "FLAG_TIME_PHASES", "MAX_D",
     "MERGE_EDGES",
     "MERGE_NONE", "MERGE_TILES", "dbscan_abi_version", "dbscan_fit",
-    "dbscan_fit_counts",
+    "dbscan_fit_counts", "dbscan_fit_device_noalloc", "ERR_TOO_LARGE",
+    "NOALLOC_SCRATCH_BYTES",
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_info",
     "dbscan_status_string", "dbscan_workspace_bytes",
     "dbscan_workspace_bytes_with_edges", "dbscan_relabel_device",
@@ -41,7 +42,7 @@ def __getattr__(name):
 
 __all__ = [
     "DbscanError", "Workspace", "fit", "fit_host", "dbscan_fit",
-    "dbscan_fit_counts",
+    "dbscan_fit_counts", "dbscan_fit_device_noalloc",
     "dbscan_fit_device", "dbscan_fit_device_ex", "dbscan_workspace_bytes",
     "dbscan_workspace_bytes_with_edges", "dbscan_status_string",
     "dbscan_abi_version", "dbscan_info", "relabel",

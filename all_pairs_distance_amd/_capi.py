@@ -20,6 +20,8 @@ ERR_OOM = -4
 ERR_WORKSPACE = -5
 ERR_HIP = -6
 ERR_CAPACITY = -7
+ERR_TOO_LARGE = -8
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MERGE_NONE, MERGE_EDGES, MERGE_TILES = 0, 1, 2
 FLAG_TIME_PHASES = 0x1
@@ -83,6 +85,9 @@ def _load() -> ctypes.CDLL:
                                          ctypes.c_size_t, vp, ctypes.c_uint32,
                                          ctypes.POINTER(dbscan_info)]
     lib.dbscan_fit_device_ex.restype = ctypes.c_int
+    lib.dbscan_fit_device_noalloc.argtypes = [vp, i64, i32, f32, i32, vp,
+                                              vp, vp]
+    lib.dbscan_fit_device_noalloc.restype = ctypes.c_int
     lib.dbscan_fit.argtypes = [vp, i64, i32, f32, i32, vp]
     lib.dbscan_fit.restype = ctypes.c_int
     lib.dbscan_fit_counts.argtypes = [vp, i64, i32, f32, i32, vp, vp]
@@ -135,6 +140,16 @@ def dbscan_fit_device_ex(d_points: int, n: int, d: int, eps: float,
         d_points, n, d, eps, min_pts, d_labels, d_counts, d_workspace,
         workspace_bytes, hip_stream, flags,
         ctypes.byref(info) if info is not None else None))
+
+
+def dbscan_fit_device_noalloc(d_points: int, n: int, d: int, eps: float,
+                              min_pts: int, d_labels: int,
+                              d_counts: int | None,
+                              hip_stream: int | None) -> int:
+    """Device-pointer fit in the library's fixed per-GPU scratch (no
+    workspace, no allocation)."""
+    return int(lib.dbscan_fit_device_noalloc(d_points, n, d, eps, min_pts,
+                                             d_labels, d_counts, hip_stream))
 
 
 def dbscan_fit(points: int, n: int, d: int, eps: float, min_pts: int,

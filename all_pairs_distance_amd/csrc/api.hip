@@ -3,6 +3,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 
 #include "dbscan.h"
@@ -247,6 +248,39 @@ bool carve_graph(Layout& L, GraphLayout& G, void* ws, size_t ws_bytes) {
   return true;
 }
 
+// ---- fixed scratch of the no-allocation entry point ------------------------
+// One copy of this array lives on every GPU the library runs on, from the
+// code object's load until the process ends.  In host code its name is a
+// host-side stand-in, not a device address: the device address of the
+// current GPU's copy comes from hipGetSymbolAddress, once per device, and
+// only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DBSCAN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch`, looked up on this device's first
+// call and kept.
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return map_hip(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return DBSCAN_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return e != hipSuccess ? map_hip(e) : DBSCAN_ERR_HIP;
+    }
+    scratch_addr[dev] = ptr;
+  }
+  *out = scratch_addr[dev];
+  return DBSCAN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,6 +309,8 @@ const char* dbscan_status_string(int status) {
     case DBSCAN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case DBSCAN_ERR_HIP: return "HIP runtime error";
     case DBSCAN_ERR_CAPACITY: return "output buffer too small (size reported)";
+    case DBSCAN_ERR_TOO_LARGE:
+      return "input too large for the fixed scratch of the no-allocation entry";
     default: return "unknown status";
   }
 }
@@ -464,6 +500,28 @@ int dbscan_fit_counts(const float* points, int64_t n, int32_t d, float eps,
 int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
                int32_t min_pts, int32_t* labels) {
   return dbscan_fit_counts(points, n, d, eps, min_pts, labels, nullptr);
+}
+
+int dbscan_fit_device_noalloc(const float* d_points, int64_t n, int32_t d,
+                              float eps, int32_t min_pts, int32_t* d_labels,
+                              int32_t* d_counts, void* hip_stream) {
+  int st = check_args(n, d, eps, min_pts);
+  if (st != DBSCAN_OK) return st;
+  if (n > 0 && (d_points == nullptr || d_labels == nullptr))
+    return DBSCAN_ERR_INVALID_ARG;
+  if (n == 0) return DBSCAN_OK;
+  if (dbscan_workspace_bytes(n, d) > (size_t)DBSCAN_NOALLOC_SCRATCH_BYTES)
+    return DBSCAN_ERR_TOO_LARGE;
+  st = have_device();
+  if (st != DBSCAN_OK) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != DBSCAN_OK) return st;
+  // the scratch beyond the fit's minimum is its edge area; the fit clears
+  // what must start at zero (status block, counts, forest) itself
+  return dbscan_fit_device_ex(d_points, n, d, eps, min_pts, d_labels,
+                              d_counts, ws, (size_t)DBSCAN_NOALLOC_SCRATCH_BYTES,
+                              hip_stream, 0u, nullptr);
 }
 
 size_t dbscan_graph_workspace_bytes(int64_t n, int32_t d, int64_t max_pairs) {

@@ -56,9 +56,12 @@ typedef enum dbscan_status {
   DBSCAN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than
                                   dbscan_workspace_bytes(n, d), or misaligned */
   DBSCAN_ERR_HIP = -6,         /* any other HIP runtime error */
-  DBSCAN_ERR_CAPACITY = -7     /* dbscan_graph_device only: the caller's
+  DBSCAN_ERR_CAPACITY = -7,    /* dbscan_graph_device only: the caller's
                                   col_idx buffer is smaller than the graph
                                   (the call reports the size needed) */
+  DBSCAN_ERR_TOO_LARGE = -8    /* dbscan_fit_device_noalloc only:
+                                  dbscan_workspace_bytes(n, d) exceeds
+                                  DBSCAN_NOALLOC_SCRATCH_BYTES */
 } dbscan_status;
 
 /* Merge strategies a fit may take (reported in dbscan_info.merge_mode). */
@@ -211,6 +214,28 @@ int dbscan_fit(const float* points, int64_t n, int32_t d, float eps,
  * dbscan_fit). */
 int dbscan_fit_counts(const float* points, int64_t n, int32_t d, float eps,
                       int32_t min_pts, int32_t* labels, int32_t* counts);
+
+/* Device scratch the no-allocation entry point works in, per GPU. */
+#define DBSCAN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same fit as dbscan_fit_device (same results, same arguments minus the
+ * workspace), worked in a fixed scratch array of
+ * DBSCAN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends; the call itself allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine).  Inputs whose
+ * dbscan_workspace_bytes(n, d) exceeds that size are refused with
+ * DBSCAN_ERR_TOO_LARGE before any device work; the scratch beyond that
+ * minimum serves as the edge area, so the merge reuses the count pass's
+ * pairs when they fit.  Every call on one GPU shares that GPU's scratch,
+ * which keeps the last call's contents (a fit clears what it needs
+ * cleared): calls that overlap in time on one GPU, from any stream or
+ * thread, race and must be serialised by the caller.  Synchronises
+ * hip_stream once before returning, as dbscan_fit_device does. */
+int dbscan_fit_device_noalloc(const float* d_points, int64_t n, int32_t d,
+                              float eps, int32_t min_pts, int32_t* d_labels,
+                              int32_t* d_counts, void* hip_stream);
 
 /* Contiguous cluster ids from the labels of a fit: clusters are numbered
  * 0..K-1 in ascending order of their label (their smallest member, so the

@@ -116,13 +116,36 @@ def test_abi_version_and_constants():
         assert getattr(_capi, name) == int(value.rstrip("u"), 0)
 
 
+def test_noalloc_scratch_size_matches_header():
+    text = open(_capi.HEADER_PATH).read()
+    m = re.search(r"#define DBSCAN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _capi.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_before_device_work():
+    x = np.zeros((8, 2), np.float32)
+    lab = np.empty(8, np.int32)
+    f = apd.dbscan_fit_device_noalloc
+    assert f(x.ctypes.data, 8, 2, 0.1, 0, lab.ctypes.data, None, None) == _capi.ERR_INVALID_ARG
+    assert f(x.ctypes.data, 8, 65, 0.1, 1, lab.ctypes.data, None, None) == _capi.ERR_INVALID_ARG
+    assert f(None, 8, 2, 0.1, 1, lab.ctypes.data, None, None) == _capi.ERR_INVALID_ARG
+    assert f(x.ctypes.data, 8, 2, 0.1, 1, None, None, None) == _capi.ERR_INVALID_ARG
+    assert f(None, 0, 2, 0.1, 1, None, None, None) == _capi.OK
+    # the first size past the fixed scratch is refused, whatever the device
+    big = 1
+    while apd.dbscan_workspace_bytes(big, 64) <= _capi.NOALLOC_SCRATCH_BYTES:
+        big *= 2
+    assert f(x.ctypes.data, big, 64, 0.1, 1, lab.ctypes.data, None, None) == \
+        _capi.ERR_TOO_LARGE
+
+
 def test_info_struct_matches_header_layout():
     # 7 int64, 2 int32, 6 float, 2 int32
     assert ctypes.sizeof(_capi.dbscan_info) == 7 * 8 + 2 * 4 + 6 * 4 + 2 * 4
 
 
 def test_status_strings():
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert isinstance(apd.dbscan_status_string(s), str)
     assert apd.dbscan_status_string(0) == "ok"
     assert "unknown" in apd.dbscan_status_string(12345)
@@ -253,3 +276,7 @@ def test_no_device_reported():
         apd.fit_host(x, 0.1, 1)
     assert e.value.status == _capi.ERR_NO_DEVICE
     assert _graph_status(x, 8, 2, 0.1) == _capi.ERR_NO_DEVICE
+    lab = np.empty(8, np.int32)
+    assert apd.dbscan_fit_device_noalloc(x.ctypes.data, 8, 2, 0.1, 1,
+                                         lab.ctypes.data, None, None) == \
+        _capi.ERR_NO_DEVICE
