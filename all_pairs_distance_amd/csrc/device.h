@@ -246,25 +246,50 @@ __device__ inline int uf_find(int* parent, int x) {
 }
 
 // Link the components of a and b: CAS the larger root under the smaller.
-__device__ inline void uf_union(int* parent, int a, int b) {
+// The two walks up the forest go in lockstep, so their loads are
+// independent and each step costs one round trip for both; the walk stops
+// as soon as both sides reach the same node (connected) or two distinct
+// roots (link them).  No pointer is rewritten on the way up: on dense
+// sets every find ends at a few hot roots, and per-step stores there (path
+// halving or splitting) made the merge up to 4x slower on a 50k-point set.
+// Only the two start nodes are pointed at the node their walk reached,
+// which keeps the trees shallow for the many later pairs that share them.
+// Every such store writes a smaller node of the same set into a non-root
+// (a walk only leaves a node that was seen as a non-root, and a node never
+// becomes a root again), so roots still change only through the CAS.
+__device__ inline void uf_union(int* parent, int a0, int b0) {
+  int a = a0, b = b0;
+  int pa = uf_load(parent + a), pb = uf_load(parent + b);
   while (true) {
-    a = uf_find(parent, a);
-    b = uf_find(parent, b);
-    if (a == b) return;
-    int hi = a > b ? a : b;
-    int lo = a > b ? b : a;
-    // A cached walk often ends at a root that was hung elsewhere meanwhile.
-    // One coherent load of its parent skips such a doomed CAS: device-scope
-    // CAS on a few hot words serialise (measured: 96% of them failed on a
-    // dense 50k-point set, and the merge ran 5x slower).
-    const int cur =
-        __hip_atomic_load(parent + hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int old = cur == hi ? atomicCAS(parent + hi, hi, lo) : cur;
-    if (old == hi) return;
-    // hi stopped being a root meanwhile; retry from the current ancestors
-    a = old;
-    b = lo;
+    if (pa == pb) break;  // a common ancestor: already connected
+    const bool ra = pa == a, rb = pb == b;
+    if (ra && rb) {
+      const int hi = a > b ? a : b;
+      const int lo = a > b ? b : a;
+      // A cached walk often ends at a root that was hung elsewhere
+      // meanwhile.  One coherent load of its parent skips such a doomed
+      // CAS: device-scope CAS on a few hot words serialise.
+      const int cur = __hip_atomic_load(parent + hi, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      const int old = cur == hi ? atomicCAS(parent + hi, hi, lo) : cur;
+      if (old == hi) {
+        pa = pb = lo;
+        break;
+      }
+      // hi stopped being a root meanwhile: continue from its new parent
+      if (hi == a) pa = old;
+      else pb = old;
+      continue;
+    }
+    if (!ra) a = pa;
+    if (!rb) b = pb;
+    const int qa = ra ? pa : uf_load(parent + a);
+    const int qb = rb ? pb : uf_load(parent + b);
+    pa = qa;
+    pb = qb;
   }
+  if (a0 != pa && uf_load(parent + a0) > pa) uf_store(parent + a0, pa);
+  if (b0 != pb && uf_load(parent + b0) > pb) uf_store(parent + b0, pb);
 }
 
 }  // namespace dbk
