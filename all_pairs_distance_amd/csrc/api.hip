@@ -19,8 +19,9 @@ int pick_dim(int d) {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-static int64_t pad_points(int64_t n) {
-  return (n + kPadPoints - 1) / kPadPoints * kPadPoints;
+static int64_t pad_points(int64_t n, int D) {
+  const int64_t m = pad_multiple(D);
+  return (n + m - 1) / m * m;
 }
 
 static size_t sort_bytes(int64_t n_pad) {
@@ -81,7 +82,7 @@ static size_t regions(int64_t n_pad, int D, size_t* out) {
 size_t layout_min_bytes(int64_t n, int d) {
   const int D = pick_dim(d);
   if (n < 0 || n > INT32_MAX || D == 0) return 0;
-  return regions(pad_points(n < 1 ? 1 : n), D, nullptr);
+  return regions(pad_points(n < 1 ? 1 : n, D), D, nullptr);
 }
 
 bool carve(Layout& L, void* ws, size_t ws_bytes) {
@@ -344,7 +345,7 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   L.d = d;
   L.D = pick_dim(d);
   L.stride = row_stride(L.D);
-  L.n_pad = pad_points(n);
+  L.n_pad = pad_points(n, L.D);
   L.expanded = (flags & DBSCAN_FLAG_EXPANDED) != 0;
   if (!carve(L, d_workspace, workspace_bytes)) return DBSCAN_ERR_WORKSPACE;
 
@@ -527,7 +528,7 @@ int dbscan_fit_device_noalloc(const float* d_points, int64_t n, int32_t d,
 size_t dbscan_graph_workspace_bytes(int64_t n, int32_t d, int64_t max_pairs) {
   const size_t base = dbscan_workspace_bytes(n, d);
   if (base == 0 || max_pairs < 0) return 0;
-  const int64_t n_pad = pad_points(n < 1 ? 1 : n);
+  const int64_t n_pad = pad_points(n < 1 ? 1 : n, pick_dim(d));
   return base + graph_fixed_bytes(n_pad) +
          align_up((size_t)n_pad * sizeof(int) + (size_t)max_pairs * sizeof(uint2),
                   256);
@@ -569,7 +570,7 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   L.d = d;
   L.D = pick_dim(d);
   L.stride = row_stride(L.D);
-  L.n_pad = pad_points(n);
+  L.n_pad = pad_points(n, L.D);
   L.expanded = (flags & DBSCAN_FLAG_EXPANDED) != 0;
   if (!carve_graph(L, G, d_workspace, workspace_bytes))
     return DBSCAN_ERR_WORKSPACE;

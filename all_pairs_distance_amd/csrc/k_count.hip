@@ -174,8 +174,30 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
         float xr[D];
 #pragma unroll
         for (int k = 0; k < D; ++k) xr[k] = rp[k];
+        if constexpr (D <= 3) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) val[p] = dist2<D>(xr, xc[p]);
+          for (int p = 0; p < P; ++p) val[p] = dist2<D>(xr, xc[p]);
+        } else {
+          // wider points: the P groups interleaved dimension by dimension
+          // (each group's sum still in ascending k, so the same bits), which
+          // gives the scheduler P independent chains instead of one (200k x
+          // 8: 1.8% faster; at width 3 the per-group order is faster)
+          float t[P];
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            t[p] = xr[0] - xc[p][0];
+            val[p] = t[p] * t[p];
+          }
+#pragma unroll
+          for (int k = 1; k < D; ++k) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) t[p] = xr[k] - xc[p][k];
+#pragma unroll
+            for (int p = 0; p < P; ++p) t[p] = t[p] * t[p];
+#pragma unroll
+            for (int p = 0; p < P; ++p) val[p] = val[p] + t[p];
+          }
+        }
       }
       // Most rows have no neighbour among these 64*P columns: one compare
       // of the lane's smallest value settles that for all P groups (min
