@@ -378,9 +378,15 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   // The merge is chosen on the device from the pair count: the edge merge,
   // then the core compaction and the tile merge, each of which exits at
   // once when it is not the one taken.  No host round trip until the end.
+  // An edge area that holds every pair i<j can never overflow: then the
+  // tile merge is not enqueued at all (two launches less per fit).
+  const bool tiles_possible =
+      !want_edges || 0.5 * (double)n * (double)(n - 1) > (double)L.edge_cap;
   if (want_edges) DB_TRY(launch_merge_edges(L, walk, stream));
-  DB_TRY(launch_compact(L, want_edges, stream));
-  DB_TRY(launch_merge_tiles(L, eps2, want_edges, walk, stream));
+  if (tiles_possible) {
+    DB_TRY(launch_compact(L, want_edges, stream));
+    DB_TRY(launch_merge_tiles(L, eps2, want_edges, walk, stream));
+  }
   tm.mark(4);
   DB_TRY(launch_label(L, d_labels, stream));
   tm.mark(5);
