@@ -375,18 +375,17 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   tm.mark(2);
   DB_TRY(launch_core(L, min_pts, d_counts, stream));
   tm.mark(3);
-  // The merge is chosen on the device from the pair count: the edge merge,
-  // then the core compaction and the tile merge, each of which exits at
-  // once when it is not the one taken.  No host round trip until the end.
+  // The merge is chosen on the device from the pair count: one launch
+  // links the recorded pairs or compacts the cores for the tile merge,
+  // which follows and exits at once when it is not needed.  No host round
+  // trip until the end.
   // An edge area that holds every pair i<j can never overflow: then the
-  // tile merge is not enqueued at all (two launches less per fit).
+  // tile merge is not enqueued at all.
   const bool tiles_possible =
       !want_edges || 0.5 * (double)n * (double)(n - 1) > (double)L.edge_cap;
-  if (want_edges) DB_TRY(launch_merge_edges(L, walk, stream));
-  if (tiles_possible) {
-    DB_TRY(launch_compact(L, want_edges, stream));
+  DB_TRY(launch_merge_edges(L, want_edges, walk, stream));
+  if (tiles_possible)
     DB_TRY(launch_merge_tiles(L, eps2, want_edges, walk, stream));
-  }
   tm.mark(4);
   DB_TRY(launch_label(L, d_labels, stream));
   tm.mark(5);

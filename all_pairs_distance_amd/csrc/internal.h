@@ -156,11 +156,12 @@ size_t prune_sort_bytes(int64_t n_pad);
 hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s);
 hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
                        hipStream_t s);
-// The merge is chosen on the device (tile_merge_needed): the edge merge,
-// the core compaction and the tile merge are all enqueued, and the ones
-// not taken exit at once.  want_edges: an edge area was offered.
-hipError_t launch_compact(const Layout& L, bool want_edges, hipStream_t s);
-hipError_t launch_merge_edges(const Layout& L, Walk walk, hipStream_t s);
+// The merge is chosen on the device (tile_merge_needed): one launch links
+// the recorded pairs or, when they overflowed, compacts the core points;
+// the tile merge after it exits at once unless it is needed.  want_edges:
+// an edge area was offered.
+hipError_t launch_merge_edges(const Layout& L, bool want_edges, Walk walk,
+                              hipStream_t s);
 hipError_t launch_merge_tiles(const Layout& L, float eps2, bool want_edges,
                               Walk walk, hipStream_t s);
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);

@@ -320,7 +320,7 @@ template <int D, bool EDGES, bool PRUNED, bool SCREEN, int PP = lane_points(D)>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_count(
     const float* __restrict__ pts, int64_t nb, int chunks_log2, int rows,
-    int64_t items, float eps2, unsigned* __restrict__ count,
+    int64_t items, int64_t n_real, float eps2, unsigned* __restrict__ count,
     uint2* __restrict__ edges, unsigned long long cap,
     unsigned long long* __restrict__ counter,
     const uint2* __restrict__ tiles, const unsigned long long* n_tiles,
@@ -368,14 +368,22 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_co
     }
     const int64_t row0 = I * T + (int64_t)c * rows;
     const int64_t colw = J * T + (int64_t)wave * 64 * P;
+    // Padding points (index >= n; in the sorted order of a pruned pass
+    // they sort last) are NaN and never neighbours: a wave whose columns
+    // are all padding skips the item, and the rows stop at the first
+    // 64-row chunk past n.  At 50,000 points of width 2 (padded to 53,248)
+    // this leaves 0.4% padding pairs instead of 11.8%.
+    if (colw >= n_real || row0 >= n_real) continue;
+    const int64_t left = n_real - row0;
+    const int rows_eff = left < rows ? (int)((left + 63) & ~(int64_t)63) : rows;
     if (I == J)
       count_item<D, P, true, EDGES, PRUNED, SCREEN>(
-          pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, box_thr, srow, ncol, nexp, rows_lds);
+          pts, row0, rows_eff, colw, eps2, count, stage, fill, sink, perm,
+          boxes64, boxes_w, box_thr, srow, ncol, nexp, rows_lds);
     else
       count_item<D, P, false, EDGES, PRUNED, SCREEN>(
-          pts, row0, rows, colw, eps2, count, stage, fill, sink, perm, boxes64,
-          boxes_w, box_thr, srow, ncol, nexp, rows_lds);
+          pts, row0, rows_eff, colw, eps2, count, stage, fill, sink, perm,
+          boxes64, boxes_w, box_thr, srow, ncol, nexp, rows_lds);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
@@ -396,7 +404,7 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   const float* pts = pruned ? L.sorted_pts : L.pts;
   const unsigned long long* n_tiles = &L.status->n_tiles;
 #define DBK_COUNT_ARGS                                                      \
-  pts, c.nb, c.chunks_log2, c.rows, c.items, eps2, L.count,                 \
+  pts, c.nb, c.chunks_log2, c.rows, c.items, L.n, eps2, L.count,            \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
       L.boxes_w, box_gap_threshold(eps2, row_stride(D)), L.srow, L.ncol,    \
@@ -414,7 +422,7 @@ static hipError_t launch_count_d(const Layout& L, float eps2, bool edges,
   } else if (!pruned && lane_points(D) > kSmallP && c.items < kSmallItems) {
     const CountPlan cs = plan_count(L.n_pad, 256 * kSmallP, false);
 #define DBK_SMALL_ARGS                                                      \
-  pts, cs.nb, cs.chunks_log2, cs.rows, cs.items, eps2, L.count,             \
+  pts, cs.nb, cs.chunks_log2, cs.rows, cs.items, L.n, eps2, L.count,        \
       edges ? L.edges : nullptr, edges ? L.edge_cap : 0ull,                 \
       &L.status->n_edges, L.tiles, n_tiles, L.tile_cap, L.perm, L.boxes64,  \
       L.boxes_w, 0.f, L.srow, L.ncol, nullptr, walk_args(walk, cs.items),  \

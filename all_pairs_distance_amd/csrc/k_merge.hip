@@ -26,17 +26,46 @@
 
 namespace dbk {
 
-// Grid-stride over the recorded pairs; their number is read from the
-// status block (the host never waits for it).  Exits at once when the
-// pairs overflowed the edge area (the tile merge runs instead) or there is
-// no core point.
-__global__ void k_merge_edges(const uint2* __restrict__ edges,
-                              unsigned long long edge_cap,
-                              const unsigned char* __restrict__ core,
-                              int* parent, int* __restrict__ bmin,
-                              const Status* __restrict__ st, WalkArgs walk) {
+// One launch for what precedes the tile merge or replaces it, chosen on
+// the device from the status block (the host never waits for it):
+//   - the pairs fit the edge area: link them (grid-stride over the pairs);
+//   - they overflowed it, or no edge area was offered: compact the core
+//     points for the tile merge that follows (each block of 1024 points
+//     writes its cores in index order at the offset k_scan_totals gave
+//     it);
+//   - no core point: nothing to do.
+__global__ __launch_bounds__(256) void k_merge_edges(
+    const uint2* __restrict__ edges, unsigned long long edge_cap,
+    bool want_edges, const unsigned char* __restrict__ core, int* parent,
+    int* __restrict__ bmin, const Status* __restrict__ st, WalkArgs walk,
+    const float* __restrict__ pts, int S, int64_t n_pad,
+    const unsigned* __restrict__ sums, int* __restrict__ core_list,
+    float* __restrict__ core_pts) {
+  if (st->n_core == 0) return;
+  if (tile_merge_needed(st, want_edges, edge_cap)) {
+    __shared__ unsigned sh[4];
+    for (int64_t blk = blockIdx.x; blk < n_pad / 1024; blk += gridDim.x) {
+      const int64_t base = blk * 1024 + threadIdx.x * 4;
+      const unsigned f4 = *reinterpret_cast<const unsigned*>(core + base);
+      unsigned f[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = (f4 >> (8 * q)) & 0xffu;
+      unsigned tot;
+      unsigned pos = sums[blk] +
+                     block_excl_scan(f[0] + f[1] + f[2] + f[3], sh, &tot);
+      for (int q = 0; q < 4; ++q) {
+        if (f[q]) {
+          const int64_t i = base + q;
+          core_list[pos] = (int)i;
+          for (int k = 0; k < S; ++k)
+            core_pts[(int64_t)pos * S + k] = pts[i * S + k];
+          ++pos;
+        }
+      }
+    }
+    return;
+  }
   const unsigned long long ne = st->n_edges;
-  if (ne > edge_cap || st->n_core == 0) return;
   // (a test mode walks the pairs in another order: results must not
   // change)
   walk_refit((int64_t)ne, walk.mul, walk.add);
@@ -61,13 +90,17 @@ __global__ void k_merge_edges(const uint2* __restrict__ edges,
 // 256 threads); the pair count is only known on the device.
 constexpr unsigned kMergeGrid = 2048;
 
-hipError_t launch_merge_edges(const Layout& L, Walk walk, hipStream_t s) {
-  if (L.edge_cap == 0) return hipSuccess;
-  unsigned long long g = (L.edge_cap + 255) / 256;
+hipError_t launch_merge_edges(const Layout& L, bool want_edges, Walk walk,
+                              hipStream_t s) {
+  const unsigned long long e_cap = want_edges ? L.edge_cap : 0ull;
+  unsigned long long g = (e_cap + 255) / 256;
+  const unsigned long long nblk = (unsigned long long)L.n_pad / 1024;
+  if (g < nblk) g = nblk;
   if (g > kMergeGrid) g = kMergeGrid;
   k_merge_edges<<<(unsigned)g, 256, 0, s>>>(
-      L.edges, L.edge_cap, L.core, L.parent, L.bmin, L.status,
-      walk_args(walk, (int64_t)(L.edge_cap < 2 ? 2 : L.edge_cap)));
+      L.edges, e_cap, want_edges, L.core, L.parent, L.bmin, L.status,
+      walk_args(walk, (int64_t)(e_cap < 2 ? 2 : e_cap)), L.pts, L.stride,
+      L.n_pad, L.block_sums, L.core_list, L.core_pts);
   return hipGetLastError();
 }
 

@@ -23,13 +23,18 @@ __global__ void k_zero_status(Status* st) {
 // Copy the caller's [n][d] points into the padded [n_pad][S] layout: the
 // coordinates d..S-1 of a real point are 0 (adding 0 to a sum of squares
 // is exact), every coordinate of a padding row is NaN (never a neighbour
-// of anything).  Flags any non-finite input coordinate.
+// of anything).  Flags any non-finite input coordinate.  The same launch
+// initialises the per-point arrays: counts 0, every point its own root,
+// no border or member minimum yet.
 __global__ void k_layout(const float* __restrict__ in, int64_t n, int d, int S,
                          int64_t total, float* __restrict__ pts,
-                         Status* __restrict__ st) {
+                         Status* __restrict__ st, int64_t n_pad,
+                         unsigned* __restrict__ count, int* __restrict__ parent,
+                         int* __restrict__ bmin, int* __restrict__ cmin) {
   bool bad = false;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  for (int64_t e = t0; e < total; e += stride) {
     const int64_t i = e / S;
     const int k = (int)(e - i * S);
     float v;
@@ -42,13 +47,7 @@ __global__ void k_layout(const float* __restrict__ in, int64_t n, int d, int S,
     pts[e] = v;
   }
   if (bad) st->nonfinite = 1u;
-}
-
-__global__ void k_init_points(int64_t n_pad, unsigned* __restrict__ count,
-                              int* __restrict__ parent, int* __restrict__ bmin,
-                              int* __restrict__ cmin) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_pad;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = t0; i < n_pad; i += stride) {
     count[i] = 0u;
     parent[i] = (int)i;
     bmin[i] = INT_MAX;
@@ -59,10 +58,9 @@ __global__ void k_init_points(int64_t n_pad, unsigned* __restrict__ count,
 hipError_t launch_prepare(const Layout& L, const float* in, hipStream_t s) {
   k_zero_status<<<1, 64, 0, s>>>(L.status);
   const int64_t total = L.n_pad * L.stride;
-  k_layout<<<grid_for(total, 256 * 8), 256, 0, s>>>(in, L.n, L.d, L.stride,
-                                                     total, L.pts, L.status);
-  k_init_points<<<grid_for(L.n_pad, 256 * 4), 256, 0, s>>>(
-      L.n_pad, L.count, L.parent, L.bmin, L.cmin);
+  k_layout<<<grid_for(total, 256 * 8), 256, 0, s>>>(
+      in, L.n, L.d, L.stride, total, L.pts, L.status, L.n_pad, L.count,
+      L.parent, L.bmin, L.cmin);
   return hipGetLastError();
 }
 
@@ -133,43 +131,6 @@ hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
   k_core<<<(unsigned)nblk, 256, 0, s>>>(L.count, L.n, min_pts, L.core,
                                         counts_out, out_vec, L.block_sums);
   k_scan_totals<<<1, 256, 0, s>>>(L.block_sums, nblk, L.status);
-  return hipGetLastError();
-}
-
-// ---- sorted compaction of the core points (tile merge only) --------------
-// Each block of 1024 points writes its cores in index order at the offset
-// k_scan_totals gave it.  Launched on every fit that may need it; exits at
-// once when the edge merge runs or there is no core point.
-__global__ __launch_bounds__(256) void k_core_scatter(
-    const unsigned char* __restrict__ core, const float* __restrict__ pts,
-    int S, const unsigned* __restrict__ sums, int* __restrict__ core_list,
-    float* __restrict__ core_pts, const Status* __restrict__ st,
-    bool want_edges, unsigned long long edge_cap) {
-  if (st->n_core == 0 || !tile_merge_needed(st, want_edges, edge_cap)) return;
-  __shared__ unsigned sh[4];
-  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
-  const unsigned f4 = *reinterpret_cast<const unsigned*>(core + base);
-  unsigned f[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) f[q] = (f4 >> (8 * q)) & 0xffu;
-  unsigned tot;
-  unsigned pos = sums[blockIdx.x] +
-                 block_excl_scan(f[0] + f[1] + f[2] + f[3], sh, &tot);
-  for (int q = 0; q < 4; ++q) {
-    if (f[q]) {
-      const int64_t i = base + q;
-      core_list[pos] = (int)i;
-      for (int k = 0; k < S; ++k) core_pts[(int64_t)pos * S + k] = pts[i * S + k];
-      ++pos;
-    }
-  }
-}
-
-hipError_t launch_compact(const Layout& L, bool want_edges, hipStream_t s) {
-  const int64_t nblk = L.n_pad / 1024;
-  k_core_scatter<<<(unsigned)nblk, 256, 0, s>>>(
-      L.core, L.pts, L.stride, L.block_sums, L.core_list, L.core_pts,
-      L.status, want_edges, L.edge_cap);
   return hipGetLastError();
 }
 
