@@ -211,21 +211,13 @@ struct PhaseTimer {
     }                                     \
   } while (0)
 
-// Graph export: after the fit's regions come the row cursors, the
-// row-offset scan totals and the segmented-sort scratch; the rest of the
-// workspace holds the captured pairs and, once they are scattered, serves
-// as the sort's second buffer (4 bytes per graph entry: 4n + 8 per pair).
-size_t graph_sort_reserve(int64_t n_pad) {
-  size_t b = graph_sort_bytes(n_pad);
-  // the size query needs a device; without one, a generous estimate
-  if (b == 0) b = (size_t)n_pad * 16 + ((size_t)1 << 20);
-  return b;
-}
-
+// Graph export: after the fit's regions come the row cursors and the
+// row-offset scan totals; the rest of the workspace holds the captured
+// pairs and, once they are scattered, serves as the row sort's second
+// buffer (4 bytes per graph entry: 4n + 8 per pair).
 size_t graph_fixed_bytes(int64_t n_pad) {
   return align_up((size_t)n_pad * sizeof(unsigned), 256) +
-         align_up(((size_t)n_pad / 1024 + 2) * sizeof(unsigned long long), 256) +
-         align_up(graph_sort_reserve(n_pad), 256);
+         align_up(((size_t)n_pad / 1024 + 2) * sizeof(unsigned long long), 256);
 }
 
 bool carve_graph(Layout& L, GraphLayout& G, void* ws, size_t ws_bytes) {
@@ -239,9 +231,6 @@ bool carve_graph(Layout& L, GraphLayout& G, void* ws, size_t ws_bytes) {
   b += align_up((size_t)L.n_pad * sizeof(unsigned), 256);
   G.row_sums = reinterpret_cast<unsigned long long*>(b);
   b += align_up(((size_t)L.n_pad / 1024 + 2) * sizeof(unsigned long long), 256);
-  G.sort_tmp = b;
-  G.sort_bytes = graph_sort_reserve(L.n_pad);
-  b += align_up(G.sort_bytes, 256);
   const size_t rest = spare - fixed;
   G.alt = b;
   L.edges = reinterpret_cast<uint2*>(b);
@@ -579,8 +568,6 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   L.expanded = (flags & DBSCAN_FLAG_EXPANDED) != 0;
   if (!carve_graph(L, G, d_workspace, workspace_bytes))
     return DBSCAN_ERR_WORKSPACE;
-  const size_t sort_need = graph_sort_bytes(n);
-  if (sort_need > G.sort_bytes) return DBSCAN_ERR_HIP;
 
   volatile float eps_v = eps;
   const float eps2 = eps_v * eps_v;
@@ -623,18 +610,13 @@ int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,
   // every row holds its point and one entry per pair it belongs to
   if ((unsigned long long)nnz != (unsigned long long)n + 2ull * n_pairs)
     return DBSCAN_ERR_HIP;
-  if (nnz >= ((int64_t)1 << 32) || (unsigned long long)nnz > col_cap)
-    return DBSCAN_ERR_CAPACITY;
+  if ((unsigned long long)nnz > col_cap) return DBSCAN_ERR_CAPACITY;
   if (n_pairs > L.edge_cap) return DBSCAN_ERR_WORKSPACE;
 
   tm.mark(3);
   DB_TRY(launch_graph_scatter(L, G, n_pairs, d_row_ptr, d_col_idx, stream));
   tm.mark(4);
-  bool in_alt = false;
-  DB_TRY(launch_graph_sort(L, G, d_row_ptr, d_col_idx, nnz, &in_alt, stream));
-  if (in_alt)
-    DB_TRY(hipMemcpyAsync(d_col_idx, G.alt, (size_t)nnz * sizeof(int32_t),
-                          hipMemcpyDeviceToDevice, stream));
+  DB_TRY(launch_graph_sort(L, G, d_row_ptr, d_col_idx, nnz, stream));
   tm.mark(5);
   DB_TRY(hipMemcpyAsync(&host_st, L.status, sizeof(Status),
                         hipMemcpyDeviceToHost, stream));

@@ -26,7 +26,8 @@ struct Status {
   unsigned long long n_tiles;      // block pairs kept by the tile pruning
   unsigned long long ymax_bits;    // largest squared norm (fp64 bits), screen
   unsigned int screen_unsafe;      // a norm too large for the screen bound
-  unsigned int pad[5];
+  unsigned int long_rows;          // graph rows listed for the work-group sort
+  unsigned int pad[4];
 };
 static_assert(sizeof(Status) == 64, "status block is 64 bytes");
 
@@ -117,8 +118,6 @@ struct Layout {
 struct GraphLayout {
   unsigned* cursor;              // [n] next free slot of each row
   unsigned long long* row_sums;  // [n / 1024 + 1] row-offset scan
-  void* sort_tmp;                // segmented sort scratch
-  size_t sort_bytes;
   void* alt;                     // second sort buffer (overlays the pairs)
 };
 
@@ -165,7 +164,6 @@ hipError_t launch_merge_edges(const Layout& L, bool want_edges, Walk walk,
 hipError_t launch_merge_tiles(const Layout& L, float eps2, bool want_edges,
                               Walk walk, hipStream_t s);
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);
-size_t graph_sort_bytes(int64_t n);
 hipError_t launch_row_offsets(const Layout& L, const GraphLayout& G,
                               int64_t* row_ptr, int* col_idx,
                               unsigned long long col_cap, hipStream_t s);
@@ -175,6 +173,6 @@ hipError_t launch_graph_scatter(const Layout& L, const GraphLayout& G,
                                 hipStream_t s);
 hipError_t launch_graph_sort(const Layout& L, const GraphLayout& G,
                              const int64_t* row_ptr, int* col_idx, int64_t nnz,
-                             bool* in_alt, hipStream_t s);
+                             hipStream_t s);
 
 }  // namespace dbk

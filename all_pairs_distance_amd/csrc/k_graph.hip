@@ -10,9 +10,9 @@
 //   2. every row starts with the point itself, then each captured pair
 //      (i, j) lands once in row i and once in row j (an atomic cursor per
 //      row hands out the slots, in no particular order);
-//   3. a segmented radix sort (rocPRIM, one segment per row) puts every
-//      row in ascending order, which makes the result unique.
-#include <rocprim/device/device_segmented_radix_sort.hpp>
+//   3. every row is sorted in ascending order (below), which makes the
+//      result unique.
+#include <climits>
 
 #include "device.h"
 #include "internal.h"
@@ -158,21 +158,6 @@ __global__ __launch_bounds__(kThreads) void k_graph_scatter(
   }
 }
 
-static unsigned key_bits(int64_t n) {
-  unsigned b = 1;
-  while (b < 31 && ((int64_t)1 << b) < n) ++b;
-  return b;
-}
-
-size_t graph_sort_bytes(int64_t n) {
-  size_t bytes = 0;
-  rocprim::double_buffer<unsigned> keys(nullptr, nullptr);
-  const hipError_t e = rocprim::segmented_radix_sort_keys(
-      nullptr, bytes, keys, 0u, (unsigned)(n > 0 ? n : 1),
-      (const int64_t*)nullptr, (const int64_t*)nullptr, 0u, key_bits(n));
-  return e == hipSuccess ? bytes : 0;
-}
-
 hipError_t launch_row_offsets(const Layout& L, const GraphLayout& G,
                               int64_t* row_ptr, int* col_idx,
                               unsigned long long col_cap, hipStream_t s) {
@@ -199,20 +184,358 @@ hipError_t launch_graph_scatter(const Layout& L, const GraphLayout& G,
   return hipGetLastError();
 }
 
-// Rows in ascending order.  The pair area is dead once scattered and serves
-// as the sort's second buffer; *in_alt tells whether the sorted rows ended
-// there.
+// ---- row sort ------------------------------------------------------------
+// Each row holds distinct indices in [0, n) in arbitrary order; it is
+// sorted in place (the result is back in col_idx).  A bitonic network in
+// its direction-free form (every compare-exchange puts the smaller value at
+// the smaller position: each level k starts with a "flip" stage pairing
+// entry i with i ^ (k-1), then half-cleaners pair i with i ^ j for
+// j = k/4 .. 1) over the row padded with INT_MAX to M entries, each thread
+// holding E consecutive entries in registers (entry index = thread * E +
+// r).  Stages whose partner is in the same thread are plain min / max on
+// registers; partners in another lane of the wave come through DPP, the
+// LDS crossbar's swizzle or a permute; partners in another wave through
+// LDS (laid out [r][thread]) with work-group barriers.  By row length:
+//   <= 64     one wave, one entry per lane (M = 64);
+//   <= 128, 256, 512, 1024   one wave, 2, 4, 8, 16 per lane;
+//   <= 2048, 4096, 8192   one work-group of 4 waves, 8, 16, 32 per
+//             thread;
+//   longer    the work-group sorts the row's 8192-entry chunks, then merges
+//             neighbouring runs, doubling their length per pass, from
+//             col_idx to the dead pair area and back (each thread merges an
+//             equal share of the output, split by a binary search on the
+//             two runs), and copies the row back after an odd number of
+//             passes.
+// Waves take rows 16 at a time and sort those up to 1024 entries; longer
+// ones go on a list (one atomic per batch, into the row cursors, dead once
+// the pairs are scattered) for the work-group kernel.
+
+constexpr int kWaveSortMax = 1024;                 // rows sorted by one wave
+constexpr int kBlockSortMax = kThreads * 32;       // 8192: by one work-group
+
+__device__ __forceinline__ void cx(int& lo, int& hi) {
+  const int a = lo < hi ? lo : hi, b = lo < hi ? hi : lo;
+  lo = a;
+  hi = b;
+}
+
+// The value of lane (lane ^ X) of the wave, X < 64: DPP for the partners
+// inside a 16-lane row (quad permutations for 1, 2, 3; half-row mirror for
+// 7, row mirror for 15, rotation by 8 for 8), the LDS crossbar's swizzle
+// for 4, 16 and 31 (within each 32 lanes, no address operand), a permute
+// for 32 and 63.
+template <int X>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (X == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false);
+  else if constexpr (X == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false);
+  else if constexpr (X == 3) return __builtin_amdgcn_update_dpp(0, v, 0x1B, 0xf, 0xf, false);
+  else if constexpr (X == 7) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);
+  else if constexpr (X == 8) return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false);
+  else if constexpr (X == 15) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);
+  else if constexpr (X < 32) return __builtin_amdgcn_ds_swizzle(v, (X << 10) | 0x1f);
+  else return __shfl_xor(v, X, 64);
+}
+
+// Flip stage with the partner in thread t ^ X (X = k/E - 1 < 64): entry r
+// pairs with the partner's entry E-1-r.  The thread with bit HB of t clear
+// (HB = k / 2E) holds the smaller positions and keeps the minima.
+template <int E, int X>
+__device__ __forceinline__ void flip_lanes(int (&v)[E], int t) {
+  int o[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) o[r] = lane_xor<X>(v[E - 1 - r]);
+  const bool lower = (t & ((X + 1) >> 1)) == 0;
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    v[r] = lower ? (o[r] < v[r] ? o[r] : v[r]) : (o[r] > v[r] ? o[r] : v[r]);
+}
+
+// Half-cleaner with the partner in thread t ^ X (X a power of two < 64).
+template <int E, int X>
+__device__ __forceinline__ void half_lanes(int (&v)[E], int t) {
+  int o[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) o[r] = lane_xor<X>(v[r]);
+  const bool lower = (t & X) == 0;
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    v[r] = lower ? (o[r] < v[r] ? o[r] : v[r]) : (o[r] > v[r] ? o[r] : v[r]);
+}
+
+// Flip or half-cleaner with the partner in another wave (X >= 64): through
+// LDS, [r][thread].
+template <int E, int W>
+__device__ __forceinline__ void cross_waves(int (&v)[E], int t, int x,
+                                            bool flip, int* lds) {
+  constexpr int T = 64 * W;
+#pragma unroll
+  for (int r = 0; r < E; ++r) lds[r * T + t] = v[r];
+  __syncthreads();
+  const bool lower = (t & (flip ? (x + 1) >> 1 : x)) == 0;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int o = lds[(flip ? E - 1 - r : r) * T + (t ^ x)];
+    v[r] = lower ? (o < v[r] ? o : v[r]) : (o > v[r] ? o : v[r]);
+  }
+  __syncthreads();
+}
+
+// In-thread stages of level K (K <= E): the flip, then the half-cleaners.
+template <int E, int K, int J>
+__device__ __forceinline__ void thread_half(int (&v)[E]) {
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    if ((r & J) == 0) cx(v[r], v[r | J]);
+  if constexpr (J > 1) thread_half<E, K, J / 2>(v);
+}
+template <int E, int K>
+__device__ __forceinline__ void thread_level(int (&v)[E]) {
+  // flip within each block of K registers
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int p = r ^ (K - 1);
+    if ((r & (K / 2)) == 0) cx(v[r], v[p]);
+  }
+  if constexpr (K >= 4) thread_half<E, K, K / 4>(v);
+  if constexpr (2 * K <= E) thread_level<E, 2 * K>(v);
+}
+
+// Half-cleaners j < E of a level above E (in-thread, partner r ^ J).
+template <int E, int J>
+__device__ __forceinline__ void thread_cleaners(int (&v)[E]) {
+  if constexpr (J >= 1) {
+#pragma unroll
+    for (int r = 0; r < E; ++r)
+      if ((r & J) == 0) cx(v[r], v[r | J]);
+    thread_cleaners<E, J / 2>(v);
+  }
+}
+
+// Half-cleaners across lanes at thread distances JT, JT/2, .., 1.
+template <int E, int JT>
+__device__ __forceinline__ void lane_cleaners(int (&v)[E], int t) {
+  if constexpr (JT >= 1) {
+    half_lanes<E, JT>(v, t);
+    lane_cleaners<E, JT / 2>(v, t);
+  }
+}
+
+// Levels k = KT*E .. 64*E of a one-wave network, unrolled at compile time.
+template <int E, int KT>
+__device__ __forceinline__ void wave_levels(int (&v)[E], int t) {
+  flip_lanes<E, KT - 1>(v, t);
+  lane_cleaners<E, KT / 4>(v, t);
+  thread_cleaners<E, E / 2>(v);
+  if constexpr (KT < 64) wave_levels<E, 2 * KT>(v, t);
+}
+
+// Bitonic network over M = E * 64 * W entries; thread t (of 64 * W) holds
+// entries t*E .. t*E+E-1 in v; ascending on return.  One wave: every stage
+// unrolled at compile time; a work-group (32 entries per thread): the
+// levels above the thread in a loop, each stage a compile-time variant.
+template <int E, int W>
+__device__ __forceinline__ void bitonic_regs(int (&v)[E], int* lds) {
+  constexpr int T = 64 * W;
+  const int t = W == 1 ? lane_id() : (int)threadIdx.x;
+  if constexpr (E > 1) thread_level<E, 2>(v);
+  if constexpr (W == 1) {
+    wave_levels<E, 2>(v, t);
+    return;
+  }
+  for (int kt = 2; kt <= T; kt <<= 1) {   // level k = kt * E
+    switch (kt - 1) {                      // the flip: partner thread t ^ (kt-1)
+      case 1: flip_lanes<E, 1>(v, t); break;
+      case 3: flip_lanes<E, 3>(v, t); break;
+      case 7: flip_lanes<E, 7>(v, t); break;
+      case 15: flip_lanes<E, 15>(v, t); break;
+      case 31: flip_lanes<E, 31>(v, t); break;
+      case 63: flip_lanes<E, 63>(v, t); break;
+      default: cross_waves<E, W>(v, t, kt - 1, true, lds); break;
+    }
+    for (int jt = kt >> 2; jt >= 1; jt >>= 1) {  // half-cleaners across threads
+      switch (jt) {
+        case 1: half_lanes<E, 1>(v, t); break;
+        case 2: half_lanes<E, 2>(v, t); break;
+        case 4: half_lanes<E, 4>(v, t); break;
+        case 8: half_lanes<E, 8>(v, t); break;
+        case 16: half_lanes<E, 16>(v, t); break;
+        case 32: half_lanes<E, 32>(v, t); break;
+        default: cross_waves<E, W>(v, t, jt, false, lds); break;
+      }
+    }
+    thread_cleaners<E, E / 2>(v);
+  }
+}
+
+// LDS index of row entry i in the staging area: one pad word per 32
+// entries, so that thread t reading entry t*E + r (fixed r) and thread t
+// writing entry t (coalesced side) both spread over the banks.
+__device__ __forceinline__ int stage_at(int i) { return i + (i >> 5); }
+
+template <int W>
+__device__ __forceinline__ void group_sync() {
+  if (W == 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
+// Sort row[0 .. len) in place with the E-per-thread network of W waves
+// (len <= E * 64 * W).  The row moves between memory and registers through
+// the staging area st (E * 64 * W + E * 2 * W ints of LDS), so that the
+// global loads and stores are coalesced; the cross-wave stages of the
+// network reuse it.
+template <int E, int W>
+__device__ __forceinline__ void sort_row(int* row, int len, int* st) {
+  constexpr int T = 64 * W;
+  constexpr int M = E * T;
+  const int t = W == 1 ? lane_id() : (int)threadIdx.x;
+  int v[E];
+  if (E == 1) {
+    v[0] = t < len ? row[t] : INT_MAX;
+  } else {
+    for (int i = t; i < M; i += T) st[stage_at(i)] = i < len ? row[i] : INT_MAX;
+    group_sync<W>();
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = st[stage_at(t * E + r)];
+    group_sync<W>();
+  }
+  bitonic_regs<E, W>(v, st);
+  if (E == 1) {
+    if (t < len) row[t] = v[0];
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; ++r) st[stage_at(t * E + r)] = v[r];
+    group_sync<W>();
+    for (int i = t; i < len; i += T) row[i] = st[stage_at(i)];
+    group_sync<W>();
+  }
+}
+
+constexpr int kRowBatch = 16;                      // rows per wave and step
+constexpr int kWaveStage = kWaveSortMax + kWaveSortMax / 32;   // ints per wave
+
+__global__ __launch_bounds__(kThreads) void k_sort_rows_wave(
+    const int64_t* __restrict__ row_ptr, int64_t n, int* col_idx,
+    unsigned* __restrict__ long_list, Status* __restrict__ st) {
+  __shared__ int stage_all[4 * kWaveStage];
+  int* stage = stage_all + (threadIdx.x >> 6) * kWaveStage;
+  const int lane = lane_id();
+  const int64_t wave = blockIdx.x * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t b0 = wave * kRowBatch; b0 < n; b0 += waves * kRowBatch) {
+    const int64_t i = b0 + lane;
+    const int64_t len =
+        lane < kRowBatch && i < n ? row_ptr[i + 1] - row_ptr[i] : 0;
+    // the batch's long rows go on the list, one atomic for the batch
+    const uint64_t longm = ballot(len > kWaveSortMax);
+    if (longm) {
+      unsigned base = 0;
+      if (lane == 0) base = atomicAdd(&st->long_rows, (unsigned)__popcll(longm));
+      base = (unsigned)__builtin_amdgcn_readfirstlane((int)base);
+      if (len > kWaveSortMax) long_list[base + bits_below(longm)] = (unsigned)i;
+    }
+    uint64_t todo = ballot(len > 1 && len <= kWaveSortMax);
+    while (todo) {
+      const int l = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int64_t r = b0 + l;
+      const int64_t rb = row_ptr[r];
+      const int rl = (int)(row_ptr[r + 1] - rb);
+      int* row = col_idx + rb;
+      if (rl <= 64) sort_row<1, 1>(row, rl, stage);
+      else if (rl <= 128) sort_row<2, 1>(row, rl, stage);
+      else if (rl <= 256) sort_row<4, 1>(row, rl, stage);
+      else if (rl <= 512) sort_row<8, 1>(row, rl, stage);
+      else sort_row<16, 1>(row, rl, stage);
+    }
+  }
+}
+
+// Number of entries of run x (length nx) among the first d outputs of the
+// merge of x and y (ties cannot occur: the entries are distinct).
+__device__ __forceinline__ int merge_split(const int* x, int nx, const int* y,
+                                           int ny, int d) {
+  int lo = d > ny ? d - ny : 0, hi = d < nx ? d : nx;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;       // take mid from x, d - mid from y
+    if (x[mid] < y[d - mid - 1]) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kThreads) void k_sort_rows_group(
+    const int64_t* __restrict__ row_ptr, int* col_idx, int* alt,
+    const unsigned* __restrict__ long_list, const Status* __restrict__ st) {
+  __shared__ int lds[kBlockSortMax + kBlockSortMax / 32];
+  const unsigned rows = st->long_rows;
+  for (unsigned q = blockIdx.x; q < rows; q += gridDim.x) {
+    const int64_t i = long_list[q];
+    const int64_t b = row_ptr[i];
+    const int len = (int)(row_ptr[i + 1] - b);
+    int* row = col_idx + b;
+    if (len <= 2048) {
+      sort_row<8, 4>(row, len, lds);
+    } else if (len <= 4096) {
+      sort_row<16, 4>(row, len, lds);
+    } else {
+      for (int c = 0; c < len; c += kBlockSortMax) {
+        const int cl = len - c < kBlockSortMax ? len - c : kBlockSortMax;
+        sort_row<32, 4>(row + c, cl, lds);
+      }
+    }
+    __syncthreads();
+    if (len <= kBlockSortMax) continue;
+    int* src = row;
+    int* dst = alt + b;
+    for (int w = kBlockSortMax; w < len; w <<= 1) {
+      // merge runs [s, s + w) and [s + w, s + 2w) for every s
+      for (int s0 = 0; s0 < len; s0 += 2 * w) {
+        const int nx = len - s0 < w ? len - s0 : w;
+        const int rest = len - s0 - nx;
+        const int ny = rest < w ? rest : w;
+        const int* x = src + s0;
+        const int* y = x + nx;
+        int* out = dst + s0;
+        const int total = nx + ny;
+        const int per = (total + (int)blockDim.x - 1) / (int)blockDim.x;
+        const int d0 = min((int)threadIdx.x * per, total);
+        const int d1 = min(d0 + per, total);
+        int ix = merge_split(x, nx, y, ny, d0);
+        int iy = d0 - ix;
+        for (int d = d0; d < d1; ++d) {
+          const bool take_x = iy >= ny || (ix < nx && x[ix] < y[iy]);
+          out[d] = take_x ? x[ix++] : y[iy++];
+        }
+      }
+      __syncthreads();
+      int* t = src;
+      src = dst;
+      dst = t;
+    }
+    if (src != row) {
+      for (int t = threadIdx.x; t < len; t += blockDim.x) row[t] = src[t];
+      __syncthreads();
+    }
+  }
+}
+
+// Rows in ascending order, in place in col_idx.
 hipError_t launch_graph_sort(const Layout& L, const GraphLayout& G,
                              const int64_t* row_ptr, int* col_idx, int64_t nnz,
-                             bool* in_alt, hipStream_t s) {
-  rocprim::double_buffer<unsigned> keys(reinterpret_cast<unsigned*>(col_idx),
-                                        reinterpret_cast<unsigned*>(G.alt));
-  size_t bytes = G.sort_bytes;
-  const hipError_t e = rocprim::segmented_radix_sort_keys(
-      G.sort_tmp, bytes, keys, (unsigned)nnz, (unsigned)L.n, row_ptr,
-      row_ptr + 1, 0u, key_bits(L.n), s);
-  if (e != hipSuccess) return e;
-  *in_alt = keys.current() != reinterpret_cast<unsigned*>(col_idx);
+                             hipStream_t s) {
+  if (L.n == 0 || nnz == 0) return hipSuccess;
+  // one batch of kRowBatch rows per wave at first
+  int64_t g = (L.n + 4 * kRowBatch - 1) / (4 * kRowBatch);
+  if (g > kMaxGrid) g = kMaxGrid;
+  k_sort_rows_wave<<<(unsigned)g, kThreads, 0, s>>>(row_ptr, L.n, col_idx,
+                                                    G.cursor, L.status);
+  k_sort_rows_group<<<2048, kThreads, 0, s>>>(
+      row_ptr, col_idx, reinterpret_cast<int*>(G.alt), G.cursor, L.status);
   return hipGetLastError();
 }
 

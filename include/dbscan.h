@@ -281,10 +281,9 @@ int dbscan_relabel_device(const int32_t* d_labels, int64_t n, int32_t* d_ids,
  *              scatter of the pairs and ms_label the row sort.
  *   info       optional; n_edges = neighbour pairs i<j, edge_capacity =
  *              pairs the workspace holds, tiles as for a fit.
- * Returns DBSCAN_ERR_CAPACITY if nnz > col_capacity or nnz >= 2^32 (the
- * row sort indexes entries with 32 bits), then DBSCAN_ERR_WORKSPACE if the
- * pairs do not fit the workspace: a second call with the sizes reported
- * succeeds.  One distance pass per call.  Synchronises hip_stream (twice)
+ * Returns DBSCAN_ERR_CAPACITY if nnz > col_capacity, then
+ * DBSCAN_ERR_WORKSPACE if the pairs do not fit the workspace: a second call
+ * with the sizes reported succeeds.  One distance pass per call.  Synchronises hip_stream (twice)
  * before returning; not capturable into a HIP graph. */
 size_t dbscan_graph_workspace_bytes(int64_t n, int32_t d, int64_t max_pairs);
 int dbscan_graph_device(const float* d_points, int64_t n, int32_t d, float eps,

@@ -72,6 +72,30 @@ def test_graph_small_random_vs_oracle(apd, orc, flags, mode):
         assert_same_graph((got_rp, got_ci), want, f"case {t} n={x.shape} eps={eps}")
 
 
+def test_graph_long_and_mixed_rows(apd, orc):
+    """Rows of every length class of the row sort: a shuffled integer line
+    (point p at position perm[p]) with eps = 4500 gives rows of 4,501 to
+    9,001 entries (the merge passes after the 4,096-entry chunks: one pass
+    near the ends of the line, two in the middle), and a second, sparse
+    line gives rows of 1 to 3 entries (one wave per row); blobs in between
+    give rows of a few dozen to a few hundred entries."""
+    rng = np.random.default_rng(4242)
+    dense = rng.permutation(9000).astype(np.float32)
+    sparse = (1.0e6 + 4000.0 * rng.permutation(3000)).astype(np.float32)
+    mid = (1.4e7 + rng.uniform(0.0, 2.0e5, 4000)).astype(np.float32)
+    x = np.concatenate([dense, sparse, mid])
+    x = np.ascontiguousarray(x[rng.permutation(x.size)]).reshape(-1, 1)
+    want = orc.graph(x, 4500.0)
+    lengths = np.diff(want[0])
+    assert lengths.max() > 8192 and lengths.min() <= 3
+    assert np.any((lengths > 2) & (lengths <= 64))
+    assert np.any((lengths > 4096) & (lengths <= 8192))
+    assert np.any((lengths > 64) & (lengths <= 4096))
+    for flags, mode in ((0, "all_tiles"), (4, "pruned")):
+        got_rp, got_ci, _ = gpu_graph(apd, x, 4500.0, flags=flags)
+        assert_same_graph((got_rp, got_ci), want, f"long rows {mode}")
+
+
 @pytest.mark.parametrize("n", [1, 63, 65, 4095, 4097, 12289])
 def test_graph_tiles_and_ragged_tails(apd, orc, n):
     for d in (1, 2, 3, 8, 33, 64):
