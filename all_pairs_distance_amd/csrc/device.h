@@ -124,6 +124,19 @@ __device__ __forceinline__ unsigned shift_in_lane_bit(unsigned v, uint64_t mask)
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ unsigned wave_incl_sum(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const unsigned t0 = (unsigned)__builtin_amdgcn_readlane((int)v, 15);
+  const unsigned t1 = (unsigned)__builtin_amdgcn_readlane((int)v, 31);
+  const unsigned t2 = (unsigned)__builtin_amdgcn_readlane((int)v, 47);
+  const int q = lane_id() >> 4;
+  return v + (q >= 1 ? t0 : 0u) + (q >= 2 ? t1 : 0u) + (q >= 3 ? t2 : 0u);
+}
+
 __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
   unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
   unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));

@@ -96,6 +96,49 @@ def test_graph_long_and_mixed_rows(apd, orc):
         assert_same_graph((got_rp, got_ci), want, f"long rows {mode}")
 
 
+def test_graph_long_rows_above_the_bitmap_limit(apd, orc):
+    """Long rows when n is above what the LDS bitmap sort covers (491,520
+    points), so they take the work-group networks and merges.  9,000 points
+    on an integer line (eps = 4,500: rows of 4,501 to 9,001 entries) and
+    500,500 isolated points on a grid of pitch 5,000, well away from it.
+    Integer coordinates below 2^22 make every fp32 decision exact (a pair
+    of the line is a neighbour iff its positions differ by at most 4,500,
+    a grid point only neighbours itself), so every row is checked against
+    that closed form, as the oracle's own one-dimensional pin does; sampled
+    rows are also recomputed by the oracle (its all-pairs graph at this
+    size would take minutes)."""
+    rng = np.random.default_rng(777)
+    nd = 9000
+    line = np.stack([rng.permutation(nd).astype(np.float64), np.zeros(nd)], 1)
+    gx, gy = np.meshgrid(np.arange(715), np.arange(700))
+    grid = np.stack([20000.0 + 5000.0 * gx.ravel(), 5000.0 + 5000.0 * gy.ravel()], 1)
+    x = np.concatenate([line, grid]).astype(np.float32)
+    x = np.ascontiguousarray(x[rng.permutation(len(x))])
+    n, eps = len(x), 4500.0
+    assert n > 491520
+    on_line = x[:, 1] == 0.0
+    line_idx = np.nonzero(on_line)[0]
+    by_pos = np.empty(nd, np.int64)
+    by_pos[x[line_idx, 0].astype(np.int64)] = line_idx
+    lo = np.maximum(np.arange(nd) - 4500, 0)
+    hi = np.minimum(np.arange(nd) + 4500, nd - 1)
+    want_len = np.ones(n, np.int64)
+    want_len[by_pos] = hi - lo + 1
+    assert want_len.max() > 8192
+    for flags, mode in ((0, "all_tiles"), (4, "pruned")):
+        rp, ci, _ = gpu_graph(apd, x, eps, flags=flags)
+        assert rp[0] == 0 and np.array_equal(np.diff(rp), want_len), mode
+        single = np.nonzero(~on_line)[0]
+        assert np.array_equal(ci[rp[single]], single), mode
+        for p in range(nd):
+            i = by_pos[p]
+            want = np.sort(by_pos[lo[p]:hi[p] + 1])
+            assert np.array_equal(ci[rp[i]:rp[i + 1]], want), (mode, p)
+        for i in (by_pos[0], by_pos[4500], by_pos[8999], single[0], single[-1]):
+            got = ci[rp[i]:rp[i + 1]].astype(np.int64)
+            assert np.array_equal(got, orc.row_neighbours(x, eps, int(i))), (mode, i)
+
+
 @pytest.mark.parametrize("n", [1, 63, 65, 4095, 4097, 12289])
 def test_graph_tiles_and_ragged_tails(apd, orc, n):
     for d in (1, 2, 3, 8, 33, 64):
