@@ -372,7 +372,7 @@ int dbscan_fit_device_ex(const float* d_points, int64_t n, int32_t d,
   // tile merge is not enqueued at all.
   const bool tiles_possible =
       !want_edges || 0.5 * (double)n * (double)(n - 1) > (double)L.edge_cap;
-  DB_TRY(launch_merge_edges(L, want_edges, walk, stream));
+  DB_TRY(launch_merge_edges(L, want_edges, walk, prune, stream));
   if (tiles_possible)
     DB_TRY(launch_merge_tiles(L, eps2, want_edges, walk, stream));
   tm.mark(4);

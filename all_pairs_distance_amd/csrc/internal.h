@@ -158,9 +158,10 @@ hipError_t launch_core(const Layout& L, int min_pts, int* counts_out,
 // The merge is chosen on the device (tile_merge_needed): one launch links
 // the recorded pairs or, when they overflowed, compacts the core points;
 // the tile merge after it exits at once unless it is needed.  want_edges:
-// an edge area was offered.
+// an edge area was offered; spread: take the pairs in a strided chunk
+// order (for the spatially grouped pairs of a pruned pass).
 hipError_t launch_merge_edges(const Layout& L, bool want_edges, Walk walk,
-                              hipStream_t s);
+                              bool spread, hipStream_t s);
 hipError_t launch_merge_tiles(const Layout& L, float eps2, bool want_edges,
                               Walk walk, hipStream_t s);
 hipError_t launch_label(const Layout& L, int* labels, hipStream_t s);

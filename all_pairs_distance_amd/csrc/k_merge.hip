@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_merge_edges(
     int* __restrict__ bmin, const Status* __restrict__ st, WalkArgs walk,
     const float* __restrict__ pts, int S, int64_t n_pad,
     const unsigned* __restrict__ sums, int* __restrict__ core_list,
-    float* __restrict__ core_pts) {
+    float* __restrict__ core_pts, bool spread) {
   if (st->n_core == 0) return;
   if (tile_merge_needed(st, want_edges, edge_cap)) {
     __shared__ unsigned sh[4];
@@ -69,11 +69,28 @@ __global__ __launch_bounds__(256) void k_merge_edges(
   // (a test mode walks the pairs in another order: results must not
   // change)
   walk_refit((int64_t)ne, walk.mul, walk.add);
+  // With spread, wave-sized chunks of pairs are taken in a strided order
+  // (chunk c' = 16381 c mod chunks, or the next multiplier coprime with
+  // the chunk count).  The pairs of a pruned pass arrive grouped by space,
+  // so consecutive chunks mostly link points of one cluster and contend
+  // for its root; spread, concurrent chunks come from the whole set.
+  // Pruned fits: 1M x 3 merge and labels 1.24 -> 0.96 ms, 262k x 64
+  // 7.27 -> 6.66 ms; the unpruned order (neighbouring chunks sharing cache
+  // lines) keeps its own: the 262k x 64 merge went 2.45 -> 2.82 ms spread.
+  constexpr int kChunk = 64;
+  const int64_t chunks = (int64_t)((ne + kChunk - 1) / kChunk);
+  int64_t cmul = spread ? 16381 : 1, cadd = 0;
+  walk_refit(chunks, cmul, cadd);
+  const unsigned long long span = (unsigned long long)chunks * kChunk;
   for (unsigned long long k = blockIdx.x * (unsigned long long)blockDim.x +
                               threadIdx.x;
-       k < ne; k += (unsigned long long)gridDim.x * blockDim.x) {
+       k < span; k += (unsigned long long)gridDim.x * blockDim.x) {
+    const unsigned long long k2 =
+        (unsigned long long)walk_item((int64_t)(k / kChunk), chunks, cmul, cadd) *
+            kChunk + k % kChunk;
+    if (k2 >= ne) continue;
     const unsigned long long e =
-        (unsigned long long)walk_item((int64_t)k, (int64_t)ne, walk.mul, walk.add);
+        (unsigned long long)walk_item((int64_t)k2, (int64_t)ne, walk.mul, walk.add);
     const uint2 ij = edges[e];
     const int i = (int)ij.x, j = (int)ij.y;
     const bool ci = core[i] != 0, cj = core[j] != 0;
@@ -91,7 +108,7 @@ __global__ __launch_bounds__(256) void k_merge_edges(
 constexpr unsigned kMergeGrid = 2048;
 
 hipError_t launch_merge_edges(const Layout& L, bool want_edges, Walk walk,
-                              hipStream_t s) {
+                              bool spread, hipStream_t s) {
   const unsigned long long e_cap = want_edges ? L.edge_cap : 0ull;
   unsigned long long g = (e_cap + 255) / 256;
   const unsigned long long nblk = (unsigned long long)L.n_pad / 1024;
@@ -100,7 +117,7 @@ hipError_t launch_merge_edges(const Layout& L, bool want_edges, Walk walk,
   k_merge_edges<<<(unsigned)g, 256, 0, s>>>(
       L.edges, e_cap, want_edges, L.core, L.parent, L.bmin, L.status,
       walk_args(walk, (int64_t)(e_cap < 2 ? 2 : e_cap)), L.pts, L.stride,
-      L.n_pad, L.block_sums, L.core_list, L.core_pts);
+      L.n_pad, L.block_sums, L.core_list, L.core_pts, spread);
   return hipGetLastError();
 }
 
