@@ -28,12 +28,16 @@ namespace dbk {
 
 // Minimum waves per SIMD the register allocator is asked to allow (1 = no
 // constraint), chosen per width by measurement: the narrow widths fit 8
-// waves (<= 64 VGPRs) and run faster there; the wide ones would spill.  The
-// screen keeps one more value per column point (its norm) and its own
-// masks, so it is given more registers.
+// waves (<= 64 VGPRs) and run faster there; widths 48 and 64 fit 6 (80
+// VGPRs; at 64, 48 bytes of spills in the per-item setup, none in the row
+// loop): 262k x 64 count 102.0 -> 101.5 ms, pruned 19.3 -> 18.2 ms against
+// the 5 waves the allocator picks unasked.  The screen keeps one more
+// value per column point (its norm) and its own masks, so it is given
+// more registers (6 or more waves there spill in the row loop or leave
+// the allocator at 4).
 constexpr int count_waves(int D, bool edges, bool screen) {
   return screen ? (D <= 2 ? 4 : D <= 4 ? 5 : D <= 16 ? (edges ? 6 : 5) : 1)
-                : (D <= 2 ? 5 : D <= 16 ? 8 : 1);
+                : (D <= 2 ? 5 : D <= 16 ? 8 : D >= 48 ? 6 : 1);
 }
 
 // Stage the pairs (row_out, col_out) of mask m, where row and col0 + lane
