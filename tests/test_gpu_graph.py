@@ -96,11 +96,13 @@ def test_graph_long_and_mixed_rows(apd, orc):
         assert_same_graph((got_rp, got_ci), want, f"long rows {mode}")
 
 
-def test_graph_long_rows_above_the_bitmap_limit(apd, orc):
-    """Long rows when n is above what the LDS bitmap sort covers (491,520
-    points), so they take the work-group networks and merges.  9,000 points
-    on an integer line (eps = 4,500: rows of 4,501 to 9,001 entries) and
-    500,500 isolated points on a grid of pitch 5,000, well away from it.
+@pytest.mark.parametrize("n", [491520, 491521, 509500])
+def test_graph_long_rows_at_the_bitmap_limit(apd, orc, n):
+    """Long rows on both sides of the LDS bitmap sort's limit: up to 491,520
+    points (a 60 KB bitmap) the bitmap, above it the work-group networks
+    and merges.  9,000 points on an integer line (eps = 4,500: rows of
+    4,501 to 9,001 entries) and the rest isolated points on a grid of pitch
+    5,000, well away from it.
     Integer coordinates below 2^22 make every fp32 decision exact (a pair
     of the line is a neighbour iff its positions differ by at most 4,500,
     a grid point only neighbours itself), so every row is checked against
@@ -112,10 +114,10 @@ def test_graph_long_rows_above_the_bitmap_limit(apd, orc):
     line = np.stack([rng.permutation(nd).astype(np.float64), np.zeros(nd)], 1)
     gx, gy = np.meshgrid(np.arange(715), np.arange(700))
     grid = np.stack([20000.0 + 5000.0 * gx.ravel(), 5000.0 + 5000.0 * gy.ravel()], 1)
-    x = np.concatenate([line, grid]).astype(np.float32)
+    x = np.concatenate([line, grid[:n - nd]]).astype(np.float32)
     x = np.ascontiguousarray(x[rng.permutation(len(x))])
-    n, eps = len(x), 4500.0
-    assert n > 491520
+    eps = 4500.0
+    assert len(x) == n
     on_line = x[:, 1] == 0.0
     line_idx = np.nonzero(on_line)[0]
     by_pos = np.empty(nd, np.int64)
