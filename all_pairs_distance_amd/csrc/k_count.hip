@@ -224,21 +224,22 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
           }
           if (amb) {
             // some pair of this row lies inside the bound: decide the
-            // row's pairs with the exact distance (or, given its norms,
-            // the exact hoisted-norm form)
+            // pairs of each group that holds one with the exact distance
+            // (or, given its norms, the exact hoisted-norm form); the
+            // other groups keep their screened masks
             const const_float_ptr rp = (const_float_ptr)(pts + row * S);
             float xr[D];
 #pragma unroll
             for (int k = 0; k < D; ++k) xr[k] = rp[k];
-            if (!PRUNED && nexp != nullptr) {
-              const float tr = ((const_float_ptr)nexp)[row];
+            const float tr = !PRUNED && nexp != nullptr
+                                 ? ((const_float_ptr)nexp)[row] : 0.f;
 #pragma unroll
-              for (int p = 0; p < P; ++p)
+            for (int p = 0; p < P; ++p) {
+              if ((ballot(val[p] <= thr) & ~m[p]) == 0) continue;
+              if (!PRUNED && nexp != nullptr)
                 m[p] = ballot(expanded_d2<D>(xr, xc[p], tr,
                                              nexp[colw + p * 64 + lane]) <= eps2);
-            } else {
-#pragma unroll
-              for (int p = 0; p < P; ++p)
+              else
                 m[p] = ballot(dist2<D>(xr, xc[p]) <= eps2);
             }
           }
