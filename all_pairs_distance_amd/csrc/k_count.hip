@@ -33,10 +33,12 @@ namespace dbk {
 // loop): 262k x 64 count 102.0 -> 101.5 ms, pruned 19.3 -> 18.2 ms against
 // the 5 waves the allocator picks unasked.  The screen keeps one more
 // value per column point (its norm) and its own masks, so it is given
-// more registers (6 or more waves there spill in the row loop or leave
-// the allocator at 4).
-constexpr int count_waves(int D, bool edges, bool screen) {
-  return screen ? (D <= 2 ? 4 : D <= 4 ? 5 : D <= 16 ? (edges ? 6 : 5) : 1)
+// more registers: 5 waves, which its LDS (rows and pair stage, 28.5 KB per
+// work-group at width 8) allows anyway; asking for 6 left the allocator
+// at 4 (200k x 8 screened count 5.03 -> 4.80 ms with 5), and 7 or more
+// spill in the row loop.
+constexpr int count_waves(int D, bool screen) {
+  return screen ? (D <= 2 ? 4 : D <= 16 ? 5 : 1)
                 : (D <= 2 ? 5 : D <= 16 ? 8 : D >= 48 ? 6 : 1);
 }
 
@@ -355,7 +357,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 
 template <int D, bool EDGES, bool PRUNED, bool SCREEN, int PP = lane_points(D)>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(count_waves(D, EDGES, SCREEN), 8))) void k_count(
+__attribute__((amdgpu_waves_per_eu(count_waves(D, SCREEN), 8))) void k_count(
     const float* __restrict__ pts, int64_t nb, int chunks_log2, int rows,
     int64_t items, int64_t n_real, float eps2, unsigned* __restrict__ count,
     uint2* __restrict__ edges, unsigned long long cap,
