@@ -98,6 +98,23 @@ constexpr int mfma_waves(int D, bool edges) {
   return D >= 24 ? 3 : 2;
 }
 
+// (s, m) = (2 s + [v <= lo], 2 m + [v <= hi]) per lane: two compares, then
+// two adds with the compare masks as carry-in; the second compare and the
+// s_nop give the first mask's read its two wait states, the s_nop and the
+// first add the second's.
+__device__ __forceinline__ void shift_in_le2(unsigned& s, unsigned& m, float v,
+                                             float lo, float hi) {
+  uint64_t t;
+  asm("v_cmp_le_f32_e32 vcc, %3, %4\n\t"
+      "v_cmp_le_f32_e64 %2, %3, %5\n\t"
+      "s_nop 0\n\t"
+      "v_addc_co_u32_e32 %0, vcc, %0, %0, vcc\n\t"
+      "v_addc_co_u32_e64 %1, %2, %1, %1, %2"
+      : "+v"(s), "+v"(m), "=&s"(t)
+      : "v"(v), "v"(lo), "v"(hi)
+      : "vcc");
+}
+
 template <int D, bool EDGES, bool PRUNED>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
@@ -232,23 +249,28 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
       for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[g][r] = acc[g][r] + ny[g];
-      // any candidate neighbour in the block?  (min skips NaN padding)
-      float tmin = acc[0][0] - th[0].y;
+      // any candidate neighbour in the block?  The smallest value of each
+      // row minus its upper threshold (rounding is monotone, so this is
+      // the smallest of the differences; min skips NaN padding).
+      float tmin = 0.f;
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
+      for (int r = 0; r < 4; ++r) {
+        float m = acc[0][r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          tmin = __builtin_fminf(tmin, acc[g][r] - th[r].y);
+        for (int g = 1; g < NG; ++g) m = __builtin_fminf(m, acc[g][r]);
+        m = m - th[r].y;
+        tmin = r == 0 ? m : __builtin_fminf(tmin, m);
+      }
       if (!ballot(tmin <= 0.f)) continue;
       // per lane: bit 4g+r of `sure` / `maybe` for pair (row 4q+r, col g)
+      // (built from the top bit down: each step doubles the word and adds
+      // the compare's lane bit as the carry)
       unsigned sure = 0, maybe = 0;
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
+      for (int g = NG - 1; g >= 0; --g)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sure |= (acc[g][r] <= th[r].x ? 1u : 0u) << (4 * g + r);
-          maybe |= (acc[g][r] <= th[r].y ? 1u : 0u) << (4 * g + r);
-        }
+        for (int r = 3; r >= 0; --r)
+          shift_in_le2(sure, maybe, acc[g][r], th[r].x, th[r].y);
       unsigned flag = sure;
       unsigned amb = maybe & ~sure;
       uint64_t pend = ballot(amb != 0);
