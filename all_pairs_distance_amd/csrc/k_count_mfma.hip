@@ -160,8 +160,10 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
       walk_refit(items, walk.mul, walk.add);
     }
   }
+  const bool blocked = !from_list && nb >= kBlockedTileRows;
   for (int64_t step = blockIdx.x; step < items; step += gridDim.x) {
-    const int64_t item = walk_item(step, items, walk.mul, walk.add);
+    const int64_t item = walk_item(
+        blocked ? xcd_item(step, items) : step, items, walk.mul, walk.add);
     const int64_t tile = item >> chunks_log2;
     const int c = (int)(item & ((1 << chunks_log2) - 1));
     int64_t I, J;
@@ -170,7 +172,8 @@ __attribute__((amdgpu_waves_per_eu(mfma_waves(D, EDGES), 8))) void k_count_mfma(
       I = tl.x;
       J = tl.y;
     } else {
-      tile_coords(tile, nb, I, J);
+      if (blocked) tile_coords_blocked(tile, nb, I, J);
+      else tile_coords(tile, nb, I, J);
     }
     const bool diag = I == J;
     const int64_t row0 = I * T + (int64_t)c * rows;
