@@ -270,9 +270,8 @@ __device__ inline int uf_find(int* parent, int x) {
 // Every such store writes a smaller node of the same set into a non-root
 // (a walk only leaves a node that was seen as a non-root, and a node never
 // becomes a root again), so roots still change only through the CAS.
-__device__ inline void uf_union(int* parent, int a0, int b0) {
+__device__ inline void uf_union(int* parent, int a0, int b0, int pa, int pb) {
   int a = a0, b = b0;
-  int pa = uf_load(parent + a), pb = uf_load(parent + b);
   while (true) {
     if (pa == pb) break;  // a common ancestor: already connected
     const bool ra = pa == a, rb = pb == b;
@@ -303,6 +302,10 @@ __device__ inline void uf_union(int* parent, int a0, int b0) {
   }
   if (a0 != pa && uf_load(parent + a0) > pa) uf_store(parent + a0, pa);
   if (b0 != pb && uf_load(parent + b0) > pb) uf_store(parent + b0, pb);
+}
+
+__device__ inline void uf_union(int* parent, int a0, int b0) {
+  uf_union(parent, a0, b0, uf_load(parent + a0), uf_load(parent + b0));
 }
 
 }  // namespace dbk

@@ -93,12 +93,14 @@ __global__ __launch_bounds__(256) void k_merge_edges(
         (unsigned long long)walk_item((int64_t)k2, (int64_t)ne, walk.mul, walk.add);
     const uint2 ij = edges[e];
     const int i = (int)ij.x, j = (int)ij.y;
-    const bool ci = core[i] != 0, cj = core[j] != 0;
-    if (ci && cj)
-      uf_union(parent, i, j);
-    else if (ci)
+    // a non-core point's parent is -1 (set with the core flags), so the two
+    // parent loads that start a union also tell which ends are cores
+    const int pi = uf_load(parent + i), pj = uf_load(parent + j);
+    if (pi >= 0 && pj >= 0)
+      uf_union(parent, i, j, pi, pj);
+    else if (pi >= 0)
       atomicMin(bmin + j, i);
-    else if (cj)
+    else if (pj >= 0)
       atomicMin(bmin + i, j);
   }
 }
