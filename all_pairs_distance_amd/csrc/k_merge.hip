@@ -127,18 +127,18 @@ typedef const unsigned char __attribute__((address_space(4)))* const_u8_ptr;
 
 // EXPANDED: pairs are decided with the hoisted-norm form, from the norm
 // table nexp (indexed by original point).
-// Work items are (1024-row block) x (T-core column block) pairs, walked
+// Work items are (rows-row block) x (T-core column block) pairs, walked
 // grid-stride; the number of column blocks follows from the core count,
 // read on the device.  Exits at once unless the fit merges by tiles.
-template <int D, bool EXPANDED>
+template <int D, bool EXPANDED, int PP = lane_points(D)>
 __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     const float* __restrict__ pts, const float* __restrict__ core_pts,
     const int* __restrict__ core_list, const unsigned char* __restrict__ core,
-    int64_t row_blocks, float eps2, int* parent, int* __restrict__ bmin,
-    const float* __restrict__ nexp, const Status* __restrict__ st,
-    bool want_edges, unsigned long long edge_cap, WalkArgs walk_r,
-    WalkArgs walk_c) {
-  constexpr int P = lane_points(D);
+    int64_t row_blocks, int rows, float eps2, int* parent,
+    int* __restrict__ bmin, const float* __restrict__ nexp,
+    const Status* __restrict__ st, bool want_edges,
+    unsigned long long edge_cap, WalkArgs walk_r, WalkArgs walk_c) {
+  constexpr int P = PP;
   constexpr int T = 256 * P;
   constexpr int S = row_stride(D);
   const int64_t n_core = st->n_core_list;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
     const int64_t rs = item / col_blocks, cs = item - rs * col_blocks;
     const int64_t rblk = walk_item(rs, row_blocks, walk_r.mul, walk_r.add);
     const int64_t cblk = walk_item(cs, col_blocks, walk_c.mul, walk_c.add);
-    const int64_t row0 = rblk * kRowsPerItem;
+    const int64_t row0 = rblk * rows;
     const int64_t colw = cblk * T + (int64_t)wave * 64 * P;
     float xc[P][D];
     int cidx[P];
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
         xc[p][k] = real ? core_pts[c * S + k] : __builtin_nanf("");
       if (EXPANDED) pc[p] = real ? nexp[cidx[p]] : 0.f;
     }
-    for (int rb = 0; rb < kRowsPerItem; rb += 64) {
+    for (int rb = 0; rb < rows; rb += 64) {
       int rowmin = INT_MAX;  // lane l: lowest core neighbour of row rb+l
       for (int l = 0; l < 64; ++l) {
         const int64_t row = row0 + rb + l;
@@ -203,26 +203,43 @@ __global__ __launch_bounds__(kThreads) void k_merge_tiles(
   }
 }
 
-template <int D>
-static hipError_t launch_merge_tiles_d(const Layout& L, float eps2,
+// Rows per work item, halved from 1,024 (down to 64) while the plan would
+// give fewer than 4,096 items (every point a core), and one column point
+// per lane when even that is under 512 items: small sets would otherwise
+// run a handful of long work-groups (2,000 points at d = 2: 4 items, the
+// merge 4.1 ms).
+template <int D, int P>
+static hipError_t launch_merge_tiles_p(const Layout& L, float eps2,
                                        bool want_edges, Walk walk,
                                        hipStream_t s) {
-  constexpr int T = 256 * lane_points(D);
-  const int64_t row_blocks = L.n_pad / kRowsPerItem;
+  constexpr int T = 256 * P;
+  int rows = kRowsPerItem;
+  while (rows > 64 && (L.n_pad / rows) * (L.n_pad / T) < 4096) rows >>= 1;
+  const int64_t row_blocks = L.n_pad / rows;
   // sized for the most items (every point a core); the excess exits
   const int64_t most = row_blocks * (L.n_pad / T);
   const unsigned grid = (unsigned)(most < 4096 ? most : 4096);
   const WalkArgs wr = walk_args(walk, row_blocks);
   const WalkArgs wc = walk_args(walk, L.n_pad / T < 2 ? 2 : L.n_pad / T);
   if (L.expanded)
-    k_merge_tiles<D, true><<<grid, kThreads, 0, s>>>(
-        L.pts, L.core_pts, L.core_list, L.core, row_blocks, eps2, L.parent,
-        L.bmin, L.nexp, L.status, want_edges, L.edge_cap, wr, wc);
+    k_merge_tiles<D, true, P><<<grid, kThreads, 0, s>>>(
+        L.pts, L.core_pts, L.core_list, L.core, row_blocks, rows, eps2,
+        L.parent, L.bmin, L.nexp, L.status, want_edges, L.edge_cap, wr, wc);
   else
-    k_merge_tiles<D, false><<<grid, kThreads, 0, s>>>(
-        L.pts, L.core_pts, L.core_list, L.core, row_blocks, eps2, L.parent,
-        L.bmin, nullptr, L.status, want_edges, L.edge_cap, wr, wc);
+    k_merge_tiles<D, false, P><<<grid, kThreads, 0, s>>>(
+        L.pts, L.core_pts, L.core_list, L.core, row_blocks, rows, eps2,
+        L.parent, L.bmin, nullptr, L.status, want_edges, L.edge_cap, wr, wc);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_merge_tiles_d(const Layout& L, float eps2,
+                                       bool want_edges, Walk walk,
+                                       hipStream_t s) {
+  constexpr int T = 256 * lane_points(D);
+  if (lane_points(D) > 1 && (L.n_pad / 64) * (L.n_pad / T) < 512)
+    return launch_merge_tiles_p<D, 1>(L, eps2, want_edges, walk, s);
+  return launch_merge_tiles_p<D, lane_points(D)>(L, eps2, want_edges, walk, s);
 }
 
 hipError_t launch_merge_tiles(const Layout& L, float eps2, bool want_edges,
