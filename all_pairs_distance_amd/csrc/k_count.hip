@@ -129,6 +129,33 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                   : wave_boxes_apart<S>(rbox, cbox, box_thr))
         continue;
     }
+    // wide points, pruned: which of the 64 rows are provably farther than
+    // eps from every column of this wave (lane l: row rb + l against the
+    // wave's column box, in the distance's own rounded order: the bound
+    // of boxes_apart with the row as a degenerate box)
+    uint64_t far_rows = 0;
+    if (PRUNED && !SCREEN && D > 16) {
+      const const_float_ptr cb =
+          (const_float_ptr)(boxes_w + (colw / (64 * P)) * 2 * S);
+      const float4* xp = (const float4*)(pts + (row0 + rb + lane) * S);
+      float sg = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < S / 4; ++k4) {
+        const float4 x4 = xp[k4];
+        const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int k = 4 * k4 + r;
+          const float lo = cb[k], hi = cb[S + k];
+          float g = 0.f;
+          if (lo > xs[r]) g = lo - xs[r];
+          else if (xs[r] > hi) g = xs[r] - hi;
+          const float q = g * g;
+          sg = k == 0 ? q : sg + q;
+        }
+      }
+      far_rows = ballot(sg > eps2);
+    }
     int rowv = 0;  // lane l: count of row rb+l over these columns
     if (SCREEN) {
       // the 64 rows' records (-2x, lo, hi) go to the wave's LDS area with
@@ -157,6 +184,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
       const int64_t row = row0 + rb + l;
       const float* cur = next;
       next += SCREEN ? SR : S;
+      if (PRUNED && !SCREEN && D > 16 && ((far_rows >> l) & 1)) continue;
       // one value per column group: the exact distance, or the screen value
       float val[P];
       float lo = 0.f, thr = eps2;
@@ -404,6 +432,25 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, SCREEN), 8))) void k_count(
       const uint2 tl = tiles[tile];
       I = tl.x;
       J = tl.y;
+      if (!SCREEN && D > 16 && I != J) {
+        // rows from the block whose first 64-point box is wider (a heuristic:
+        // the evaluation is symmetric); far rows are then skipped row by row
+        constexpr int S = row_stride(D);
+        const float* bi = boxes_w + I * (T / (64 * P)) * 2 * S;
+        const float* bj = boxes_w + J * (T / (64 * P)) * 2 * S;
+        const int k = lane_id();
+        float ei = 0.f, ej = 0.f;
+        if (k < S) {
+          const float di = bi[S + k] - bi[k], dj = bj[S + k] - bj[k];
+          ei = di * di;
+          ej = dj * dj;
+        }
+        if (wave_sum_f32(ej) > wave_sum_f32(ei)) {
+          const int64_t t = I;
+          I = J;
+          J = t;
+        }
+      }
     } else {
       if (blocked) tile_coords_blocked(tile, nb, I, J);
       else tile_coords(tile, nb, I, J);
