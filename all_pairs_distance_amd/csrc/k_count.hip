@@ -138,8 +138,9 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
       const const_float_ptr cb =
           (const_float_ptr)(boxes_w + (colw / (64 * P)) * 2 * S);
       const float4* xp = (const float4*)(pts + (row0 + rb + lane) * S);
+      // (the sum starts from +0: adding the first square to it is exact)
       float sg = 0.f;
-#pragma unroll
+#pragma unroll 2
       for (int k4 = 0; k4 < S / 4; ++k4) {
         const float4 x4 = xp[k4];
         const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
@@ -150,8 +151,7 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
           float g = 0.f;
           if (lo > xs[r]) g = lo - xs[r];
           else if (xs[r] > hi) g = xs[r] - hi;
-          const float q = g * g;
-          sg = k == 0 ? q : sg + q;
+          sg = sg + g * g;
         }
       }
       far_rows = ballot(sg > eps2);
