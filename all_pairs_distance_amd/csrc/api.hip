@@ -24,13 +24,6 @@ static int64_t pad_points(int64_t n, int D) {
   return (n + m - 1) / m * m;
 }
 
-static size_t sort_bytes(int64_t n_pad) {
-  size_t b = prune_sort_bytes(n_pad);
-  // the size query needs a device; without one, a generous estimate
-  if (b == 0) b = (size_t)n_pad * 16 + ((size_t)1 << 20);
-  return b;
-}
-
 static int64_t tile_capacity(int64_t n_pad, int D) {
   const int64_t nb = n_pad / block_points(D);
   const int64_t all = nb * (nb + 1) / 2;
@@ -69,7 +62,7 @@ static size_t regions(int64_t n_pad, int D, size_t* out) {
       np * sizeof(float),            // ncol
       np * sizeof(float),            // nexp
       (7 * S + 1) * sizeof(float),   // pca
-      sort_bytes(n_pad),             // radix sort scratch (last)
+      prune_sort_bytes(n_pad),       // key sort counts
   };
   size_t total = 0;
   for (int r = 0; r < kRegions; ++r) {
@@ -115,8 +108,7 @@ bool carve(Layout& L, void* ws, size_t ws_bytes) {
   L.ncol = reinterpret_cast<float*>(b + off[21]);
   L.nexp = reinterpret_cast<float*>(b + off[22]);
   L.pca = reinterpret_cast<float*>(b + off[23]);
-  L.sort_tmp = b + off[24];
-  L.sort_tmp_bytes = need - off[24];
+  L.sort_hist = reinterpret_cast<unsigned*>(b + off[24]);
   L.bytes_min = need;
   const size_t spare = ws_bytes - need;
   L.edges = reinterpret_cast<uint2*>(b + need);

@@ -92,9 +92,9 @@ struct Layout {
   unsigned* block_sums;// [n_pad / 1024 + 1] compaction scan
   // tile pruning (used only when asked for)
   unsigned* bbox;      // [12] order-encoded min/max of up to 6 key coordinates
-  unsigned* keys_in;   // [n_pad] sort keys
-  unsigned* keys_out;  // [n_pad]
-  int* idx_in;         // [n_pad] 0..n_pad-1
+  unsigned* keys_in;   // [n_pad] key sort: the other key buffer
+  unsigned* keys_out;  // [n_pad] sort keys (in ascending order once sorted)
+  int* idx_in;         // [n_pad] key sort: the other index buffer
   int* perm;           // [n_pad] sorted position -> original index
   float* sorted_pts;   // [n_pad][stride] points in sorted order
   float* boxes;        // [nb][2][stride] block bounding boxes
@@ -107,8 +107,7 @@ struct Layout {
   float* ncol;         // [n_pad] fp32 squared norm of each point (screen)
   float* nexp;         // [n_pad] squared norm as the hoisted-norm form
                        //         takes it: rounded squares summed in k order
-  void* sort_tmp;      // radix sort scratch
-  size_t sort_tmp_bytes;
+  unsigned* sort_hist;  // key sort: digit totals, then per-tile counts
   uint2* edges;        // edge area (may be empty)
   unsigned long long edge_cap;
   size_t bytes_min;    // minimum workspace

@@ -21,8 +21,6 @@
 // pruning rule on the all-pairs tiles.
 #include <climits>
 
-#include <rocprim/device/device_radix_sort.hpp>
-
 #include "device.h"
 #include "internal.h"
 
@@ -46,6 +44,9 @@ __device__ __forceinline__ float ord_f(unsigned u) {
 // Most coordinates a sort key covers.
 constexpr int kKeyDims = 6;
 
+// Key sort: 8-bit digits of 32-bit keys.
+constexpr int kSortPasses = 4;
+
 // ---- sort key of wide points: principal directions --------------------
 // For points of 16 or more dimensions the key covers the coordinates along
 // the six leading principal directions of a strided sample of the points,
@@ -61,6 +62,23 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
+// sum over l of row[l] * x[l], accumulated in ascending l; x is a
+// 16-byte-aligned LDS vector that every lane reads whole (broadcasts)
+__device__ __forceinline__ float row_dot(const float (&row)[64],
+                                         const float* x) {
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const float4 c = x4[q];
+    acc += row[4 * q] * c.x;
+    acc += row[4 * q + 1] * c.y;
+    acc += row[4 * q + 2] * c.z;
+    acc += row[4 * q + 3] * c.w;
+  }
+  return acc;
+}
+
 // One workgroup of 256 threads.  out: the sample mean [S], then kKeyDims
 // orthonormal directions [S each], then the sample's mean squared residual
 // off them.
@@ -70,7 +88,7 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
   __shared__ float tile[64][65];
   __shared__ float mean[64];
   __shared__ float cov[64][65];
-  __shared__ float vs[kKeyDims][64];
+  __shared__ __attribute__((aligned(16))) float vs[kKeyDims][64];
   const int tid = threadIdx.x;
   const int64_t m = n < kPcaSample ? n : kPcaSample;
   const int64_t step = n / m;
@@ -116,9 +134,14 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
     for (int j = 0; j < 4; ++j) cov[k0 + i][l0 + j] = c[i][j];
   __syncthreads();
   // subspace iteration in wave 0: lane k holds component k of every
-  // direction; V <- orth(C V), modified Gram-Schmidt
+  // direction and row k of C (in registers; the directions are read back
+  // from LDS as broadcasts, four components a read); V <- orth(C V),
+  // modified Gram-Schmidt
   if (tid < 64) {
     const int k = tid;
+    float crow[64];
+#pragma unroll
+    for (int l = 0; l < 64; ++l) crow[l] = cov[k][l];
     float v[kKeyDims];
     for (int j = 0; j < kKeyDims; ++j)   // a fixed full-rank start
       v[j] = (k == j ? 4.f : 0.f) + (float)((k * (2 * j + 3) + j) % 7) - 3.f;
@@ -128,11 +151,7 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float w[kKeyDims];
-      for (int j = 0; j < kKeyDims; ++j) {
-        float acc = 0.f;
-        for (int l = 0; l < 64; ++l) acc += cov[k][l] * vs[j][l];
-        w[j] = acc;
-      }
+      for (int j = 0; j < kKeyDims; ++j) w[j] = row_dot(crow, vs[j]);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -153,9 +172,7 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float captured = 0.f;
     for (int j = 0; j < kKeyDims; ++j) {
-      float acc = 0.f;
-      for (int l = 0; l < 64; ++l) acc += cov[k][l] * vs[j][l];
-      cv[j] = acc;
+      cv[j] = row_dot(crow, vs[j]);
       captured += v[j] * cv[j];
     }
     captured = wave_sum_f(captured);
@@ -251,9 +268,12 @@ __global__ __launch_bounds__(256) void k_bbox(
   }
 }
 
-__global__ void k_bbox_init(unsigned* lohi, int KD) {
+// Also clears the key sort's digit totals (kSortPasses * 256 words).
+__global__ void k_bbox_init(unsigned* lohi, int KD, unsigned* totals) {
   if ((int)threadIdx.x < KD) lohi[threadIdx.x] = ~0u;
   else if ((int)threadIdx.x < 2 * KD) lohi[threadIdx.x] = 0u;
+  for (int i = threadIdx.x; i < kSortPasses * 256; i += blockDim.x)
+    totals[i] = 0u;
 }
 
 // Spread the low 10 bits of v to every third bit.
@@ -335,41 +355,194 @@ __global__ void k_gather(const float* __restrict__ pts,
 }
 
 // Bounding box of each block of T sorted points over all S coordinates;
-// padding rows are skipped, an all-padding block gets lo > hi.
+// padding rows are skipped, an all-padding block gets lo > hi.  Thread t
+// takes coordinate t % S of every G-th point of the block from point t / S
+// on (G = 256 / S groups), so a group reads whole rows, coalesced; the G
+// partial boxes are then combined in LDS.
 __global__ __launch_bounds__(256) void k_block_boxes(
     const float* __restrict__ spts, const int* __restrict__ perm, int64_t n,
     int T, int S, float* __restrict__ boxes) {
+  __shared__ float part_lo[256], part_hi[256];
   const int64_t b = blockIdx.x;
-  for (int k = 0; k < S; ++k) {
-    float lo = __builtin_inff(), hi = -__builtin_inff();
-    for (int t = threadIdx.x; t < T; t += 256) {
-      const int64_t s = b * T + t;
+  const int t = threadIdx.x, G = 256 / S, k = t % S, g = t / S;
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  if (g < G) {
+    for (int q = g; q < T; q += G) {
+      const int64_t s = b * T + q;
       if (perm[s] < n) {
         const float v = spts[s * S + k];
         lo = v < lo ? v : lo;
         hi = v > hi ? v : hi;
       }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ol = __shfl_xor(lo, off), oh = __shfl_xor(hi, off);
-      lo = ol < lo ? ol : lo;
-      hi = oh > hi ? oh : hi;
+  }
+  part_lo[t] = lo;
+  part_hi[t] = hi;
+  __syncthreads();
+  if (t < S) {
+    for (int j = 1; j < G; ++j) {
+      const float l = part_lo[j * S + t], h = part_hi[j * S + t];
+      lo = l < lo ? l : lo;
+      hi = h > hi ? h : hi;
     }
-    __shared__ float sl[4], sh[4];
-    if (lane_id() == 0) {
-      sl[threadIdx.x >> 6] = lo;
-      sh[threadIdx.x >> 6] = hi;
+    boxes[(b * 2) * S + t] = lo;
+    boxes[(b * 2 + 1) * S + t] = hi;
+  }
+}
+
+// Boxes of blocks of F consecutive 64-point groups from the groups' own
+// boxes: minima and maxima are exact, so these are the boxes of the points
+// themselves (an all-padding group, lo > hi, adds nothing).
+__global__ void k_box_union(const float* __restrict__ in, int64_t nb_out,
+                            int F, int S, float* __restrict__ out) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+       e < nb_out * S; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = e / S;
+    const int k = (int)(e - b * S);
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+    for (int f = 0; f < F; ++f) {
+      const float* src = in + (b * F + f) * 2 * S;
+      const float l = src[k], h = src[S + k];
+      lo = l < lo ? l : lo;
+      hi = h > hi ? h : hi;
+    }
+    out[(b * 2) * S + k] = lo;
+    out[(b * 2 + 1) * S + k] = hi;
+  }
+}
+
+// ---- key sort ---------------------------------------------------------------
+// A least-significant-digit radix sort of the (key, index) pairs: four
+// stable passes over 8-bit digits.  A pass cuts the keys into tiles of
+// 256 * ITEMS consecutive keys and runs three kernels:
+//   k_sort_hist     each tile counts its digits into hist[d * tiles + t];
+//   k_sort_offsets  one work-group per digit d rewrites its row of counts
+//                   as the output position of tile t's first key of digit
+//                   d: the keys of every digit below d, plus the keys of
+//                   digit d in the tiles before t;
+//   k_sort_scatter  each tile writes its keys, in input order, from there.
+// Equal digits keep their input order, so every pass is stable, and after
+// the four the keys ascend with equal keys in their input (index) order.
+// The digit totals do not depend on the order of the keys: the first
+// pass's histogram kernel sums them for all four passes.
+
+// lanes of this wave holding the same digit as this lane, valid lanes only
+// (0 for an invalid lane): eight ballots, one per digit bit
+__device__ __forceinline__ uint64_t same_digit(unsigned dig, bool valid) {
+  uint64_t peers = ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (dig >> b) & 1u;
+    const uint64_t ones = ballot(bit);
+    peers &= bit ? ones : ~ones;
+  }
+  return valid ? peers : 0ull;
+}
+
+template <int ITEMS, bool TOTALS>
+__global__ __launch_bounds__(256) void k_sort_hist(
+    const unsigned* __restrict__ keys, int64_t n, int shift, int64_t tiles,
+    unsigned* __restrict__ hist, unsigned* __restrict__ totals) {
+  constexpr int H = TOTALS ? kSortPasses * 256 : 256;
+  __shared__ unsigned h[H];
+  for (int i = threadIdx.x; i < H; i += 256) h[i] = 0u;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * 256 * ITEMS;
+  unsigned k[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int64_t g = base + r * 256 + threadIdx.x;
+    k[r] = g < n ? keys[g] : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    if (base + r * 256 + threadIdx.x >= n) continue;
+    if (TOTALS) {
+#pragma unroll
+      for (int p = 0; p < kSortPasses; ++p)
+        atomicAdd(&h[p * 256 + ((k[r] >> (8 * p)) & 255u)], 1u);
+    } else {
+      atomicAdd(&h[(k[r] >> shift) & 255u], 1u);
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  hist[(int64_t)t * tiles + blockIdx.x] = h[(TOTALS ? shift / 8 * 256 : 0) + t];
+  if (TOTALS) {
+    for (int i = t; i < H; i += 256)
+      if (h[i]) atomicAdd(&totals[i], h[i]);
+  }
+}
+
+// grid: 256 work-groups, one per digit; totals: this pass's 256 digit counts
+__global__ __launch_bounds__(256) void k_sort_offsets(
+    const unsigned* __restrict__ totals, int64_t tiles,
+    unsigned* __restrict__ hist) {
+  __shared__ unsigned sh[4];
+  __shared__ unsigned first;
+  const int dig = blockIdx.x;
+  unsigned all;
+  const unsigned below = block_excl_scan(totals[threadIdx.x], sh, &all);
+  if ((int)threadIdx.x == dig) first = below;
+  __syncthreads();
+  unsigned run = first;
+  unsigned* row = hist + (int64_t)dig * tiles;
+  for (int64_t b = 0; b < tiles; b += 256) {
+    const int64_t i = b + threadIdx.x;
+    const unsigned v = i < tiles ? row[i] : 0u;
+    unsigned sum;
+    const unsigned ex = block_excl_scan(v, sh, &sum);
+    if (i < tiles) row[i] = run + ex;
+    run += sum;
+  }
+}
+
+// Rounds of 256 keys in input order (thread t: key r*256 + t of the tile):
+// a key's place is its digit's running position, plus the keys of that
+// digit in lower waves of the round, plus those in lower lanes of its wave.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void k_sort_scatter(
+    const unsigned* __restrict__ kin, const int* __restrict__ vin, int64_t n,
+    int shift, int64_t tiles, const unsigned* __restrict__ offs,
+    unsigned* __restrict__ kout, int* __restrict__ vout) {
+  __shared__ unsigned pos[256];
+  __shared__ unsigned wcnt[4][256];
+  const int t = threadIdx.x, wave = t >> 6;
+  pos[t] = offs[(int64_t)t * tiles + blockIdx.x];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wcnt[w][t] = 0u;
+  const int64_t base = (int64_t)blockIdx.x * 256 * ITEMS;
+  unsigned k[ITEMS];
+  int v[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int64_t g = base + r * 256 + t;
+    k[r] = g < n ? kin[g] : 0u;
+    v[r] = g < n ? vin[g] : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const bool valid = base + r * 256 + t < n;
+    const unsigned dig = (k[r] >> shift) & 255u;
+    const uint64_t peers = same_digit(dig, valid);
+    const unsigned lower = bits_below(peers);
+    if (valid && lower == 0) wcnt[wave][dig] = (unsigned)__popcll(peers);
+    __syncthreads();
+    if (valid) {
+      unsigned p = pos[dig] + lower;
+      for (int w = 0; w < wave; ++w) p += wcnt[w][dig];
+      // always below n when the counts are consistent; the test keeps a
+      // mistake from writing outside the buffers
+      if (p < (uint64_t)n) {
+        kout[p] = k[r];
+        vout[p] = v[r];
+      }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float l = sl[0], h = sh[0];
-      for (int w = 1; w < 4; ++w) {
-        l = sl[w] < l ? sl[w] : l;
-        h = sh[w] > h ? sh[w] : h;
-      }
-      boxes[(b * 2) * S + k] = l;
-      boxes[(b * 2 + 1) * S + k] = h;
-    }
+    pos[t] += wcnt[0][t] + wcnt[1][t] + wcnt[2][t] + wcnt[3][t];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w][t] = 0u;
     __syncthreads();
   }
 }
@@ -418,12 +591,21 @@ __global__ void k_tile_list(const float* __restrict__ boxes, int64_t nb, int S,
   }
 }
 
+// Keys per thread per tile: 16 once that still gives a tile per compute
+// unit, else 4 (more, smaller tiles).  Measured (layout, sort and boxes of
+// a pruned fit): 50k x 2 0.146 -> 0.103 ms and 200k x 8 0.171 -> 0.143 ms
+// with 4; 1M x 3 0.246 ms with 16, 0.274 with 4.
+static int sort_items(int64_t n_pad) { return n_pad >= 256 * 4096 ? 16 : 4; }
+
+static int64_t sort_tiles(int64_t n_pad) {
+  const int64_t tile = 256 * (int64_t)sort_items(n_pad);
+  return (n_pad + tile - 1) / tile;
+}
+
 size_t prune_sort_bytes(int64_t n_pad) {
-  size_t bytes = 0;
-  (void)rocprim::radix_sort_pairs(nullptr, bytes, (unsigned*)nullptr,
-                                  (unsigned*)nullptr, (int*)nullptr,
-                                  (int*)nullptr, (size_t)n_pad, 0u, 32u);
-  return bytes;
+  // the digit totals of the four passes, then one pass's tile counts
+  return ((size_t)kSortPasses * 256 + 256 * (size_t)sort_tiles(n_pad)) *
+         sizeof(unsigned);
 }
 
 hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s) {
@@ -433,31 +615,59 @@ hipError_t launch_prune(const Layout& L, int T, float eps2, hipStream_t s) {
   const int KD = wide ? kKeyDims : (L.d < 3 ? L.d : 3);
   const float* pca = wide ? L.pca : nullptr;
   if (wide) k_pca<<<1, 256, 0, s>>>(L.pts, L.n, L.stride, L.d, L.pca);
-  k_bbox_init<<<1, 64, 0, s>>>(L.bbox, KD);
+  unsigned* totals = L.sort_hist;
+  unsigned* hist = L.sort_hist + kSortPasses * 256;
+  k_bbox_init<<<1, 256, 0, s>>>(L.bbox, KD, totals);
   // at most 512 work-groups (one atomic per bound each), 4+ points per
   // thread
   const unsigned bgrid = grid_for_p(L.n, 256 * 4);
   k_bbox<<<bgrid < 512 ? bgrid : 512, 256, 0, s>>>(L.pts, L.n, L.stride, KD,
                                                      L.d, pca, L.bbox);
+  // the keys and indices start where the fourth pass leaves them
   k_keys<<<grid_for_p(L.n_pad, 256 * 4), 256, 0, s>>>(
-      L.pts, L.n, L.n_pad, L.stride, KD, L.d, pca, L.bbox, L.keys_in,
-      L.idx_in);
-  size_t bytes = L.sort_tmp_bytes;
-  hipError_t e = rocprim::radix_sort_pairs(
-      L.sort_tmp, bytes, L.keys_in, L.keys_out, L.idx_in, L.perm,
-      (size_t)L.n_pad, 0u, 32u, s);
-  if (e != hipSuccess) return e;
+      L.pts, L.n, L.n_pad, L.stride, KD, L.d, pca, L.bbox, L.keys_out,
+      L.perm);
+  const int64_t tiles_s = sort_tiles(L.n_pad);
+  unsigned* ks = L.keys_out;
+  int* vs = L.perm;
+  unsigned* kd = L.keys_in;
+  int* vd = L.idx_in;
+  const bool wide_tiles = sort_items(L.n_pad) == 16;
+  for (int p = 0; p < kSortPasses; ++p) {
+#define DBK_SORT_PASS(IT)                                                   \
+  do {                                                                      \
+    if (p == 0)                                                             \
+      k_sort_hist<IT, true><<<(unsigned)tiles_s, 256, 0, s>>>(              \
+          ks, L.n_pad, 0, tiles_s, hist, totals);                           \
+    else                                                                    \
+      k_sort_hist<IT, false><<<(unsigned)tiles_s, 256, 0, s>>>(             \
+          ks, L.n_pad, 8 * p, tiles_s, hist, nullptr);                      \
+    k_sort_offsets<<<256, 256, 0, s>>>(totals + 256 * p, tiles_s, hist);    \
+    k_sort_scatter<IT><<<(unsigned)tiles_s, 256, 0, s>>>(                   \
+        ks, vs, L.n_pad, 8 * p, tiles_s, hist, kd, vd);                     \
+  } while (0)
+    if (wide_tiles) DBK_SORT_PASS(16);
+    else DBK_SORT_PASS(4);
+#undef DBK_SORT_PASS
+    unsigned* tk = ks;
+    ks = kd;
+    kd = tk;
+    int* tv = vs;
+    vs = vd;
+    vd = tv;
+  }
   k_gather<<<grid_for_p(L.n_pad * L.stride, 256 * 8), 256, 0, s>>>(
       L.pts, L.perm, L.n_pad * L.stride, L.stride, L.sorted_pts);
   const int64_t nb = L.n_pad / T;
-  k_block_boxes<<<(unsigned)nb, 256, 0, s>>>(L.sorted_pts, L.perm, L.n, T,
-                                             L.stride, L.boxes);
-  // finer boxes, tested inside the count pass: 64-point row groups and the
-  // 64*P columns one wave holds
+  // boxes of the 64-point row groups (tested inside the count pass), then
+  // from them those of the 64*P columns one wave holds and of the blocks
   k_block_boxes<<<(unsigned)(L.n_pad / 64), 256, 0, s>>>(
       L.sorted_pts, L.perm, L.n, 64, L.stride, L.boxes64);
-  k_block_boxes<<<(unsigned)(L.n_pad / (T / 4)), 256, 0, s>>>(
-      L.sorted_pts, L.perm, L.n, T / 4, L.stride, L.boxes_w);
+  const int64_t nw = L.n_pad / (T / 4);
+  k_box_union<<<grid_for_p(nw * L.stride, 256), 256, 0, s>>>(
+      L.boxes64, nw, T / 4 / 64, L.stride, L.boxes_w);
+  k_box_union<<<grid_for_p(nb * L.stride, 256), 256, 0, s>>>(
+      L.boxes64, nb, T / 64, L.stride, L.boxes);
   const int64_t tiles = nb * (nb + 1) / 2;
   k_tile_list<<<grid_for_p(tiles, 256), 256, 0, s>>>(
       L.boxes, nb, L.stride, eps2, L.tiles, L.tile_cap, L.status);
