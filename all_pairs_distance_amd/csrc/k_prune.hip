@@ -62,23 +62,6 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
-// sum over l of row[l] * x[l], accumulated in ascending l; x is a
-// 16-byte-aligned LDS vector that every lane reads whole (broadcasts)
-__device__ __forceinline__ float row_dot(const float (&row)[64],
-                                         const float* x) {
-  const float4* x4 = reinterpret_cast<const float4*>(x);
-  float acc = 0.f;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const float4 c = x4[q];
-    acc += row[4 * q] * c.x;
-    acc += row[4 * q + 1] * c.y;
-    acc += row[4 * q + 2] * c.z;
-    acc += row[4 * q + 3] * c.w;
-  }
-  return acc;
-}
-
 // One workgroup of 256 threads.  out: the sample mean [S], then kKeyDims
 // orthonormal directions [S each], then the sample's mean squared residual
 // off them.
@@ -88,7 +71,7 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
   __shared__ float tile[64][65];
   __shared__ float mean[64];
   __shared__ float cov[64][65];
-  __shared__ __attribute__((aligned(16))) float vs[kKeyDims][64];
+  __shared__ float vs[kKeyDims][64];
   const int tid = threadIdx.x;
   const int64_t m = n < kPcaSample ? n : kPcaSample;
   const int64_t step = n / m;
@@ -134,14 +117,9 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
     for (int j = 0; j < 4; ++j) cov[k0 + i][l0 + j] = c[i][j];
   __syncthreads();
   // subspace iteration in wave 0: lane k holds component k of every
-  // direction and row k of C (in registers; the directions are read back
-  // from LDS as broadcasts, four components a read); V <- orth(C V),
-  // modified Gram-Schmidt
+  // direction; V <- orth(C V), modified Gram-Schmidt
   if (tid < 64) {
     const int k = tid;
-    float crow[64];
-#pragma unroll
-    for (int l = 0; l < 64; ++l) crow[l] = cov[k][l];
     float v[kKeyDims];
     for (int j = 0; j < kKeyDims; ++j)   // a fixed full-rank start
       v[j] = (k == j ? 4.f : 0.f) + (float)((k * (2 * j + 3) + j) % 7) - 3.f;
@@ -151,7 +129,11 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float w[kKeyDims];
-      for (int j = 0; j < kKeyDims; ++j) w[j] = row_dot(crow, vs[j]);
+      for (int j = 0; j < kKeyDims; ++j) {
+        float acc = 0.f;
+        for (int l = 0; l < 64; ++l) acc += cov[k][l] * vs[j][l];
+        w[j] = acc;
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -172,7 +154,9 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float captured = 0.f;
     for (int j = 0; j < kKeyDims; ++j) {
-      cv[j] = row_dot(crow, vs[j]);
+      float acc = 0.f;
+      for (int l = 0; l < 64; ++l) acc += cov[k][l] * vs[j][l];
+      cv[j] = acc;
       captured += v[j] * cv[j];
     }
     captured = wave_sum_f(captured);
@@ -591,11 +575,11 @@ __global__ void k_tile_list(const float* __restrict__ boxes, int64_t nb, int S,
   }
 }
 
-// Keys per thread per tile: 16 once that still gives a tile per compute
-// unit, else 4 (more, smaller tiles).  Measured (layout, sort and boxes of
-// a pruned fit): 50k x 2 0.146 -> 0.103 ms and 200k x 8 0.171 -> 0.143 ms
-// with 4; 1M x 3 0.246 ms with 16, 0.274 with 4.
-static int sort_items(int64_t n_pad) { return n_pad >= 256 * 4096 ? 16 : 4; }
+// Keys per thread per tile: 16 from 786,432 keys on (192 or more tiles of
+// 4,096), else 4 (more, smaller tiles).  Measured (layout, sort and boxes
+// of a pruned fit): 50k x 2 0.146 -> 0.103 ms and 200k x 8 0.171 -> 0.143
+// ms with 4; 1M x 3 0.246 ms with 16, 0.274 with 4.
+static int sort_items(int64_t n_pad) { return n_pad >= 3 * (1 << 18) ? 16 : 4; }
 
 static int64_t sort_tiles(int64_t n_pad) {
   const int64_t tile = 256 * (int64_t)sort_items(n_pad);
