@@ -174,6 +174,32 @@ def test_degenerate_inputs(apd, orc):
     assert_same(lab, cnt, want_l, want_c, "minpts 1")
 
 
+def test_pruned_key_sort_edge_cases(apd, orc):
+    """The pruned mode's key sort on keys that are all equal, descending,
+    or drawn from a few values: any permutation gives the same results,
+    and a wrong one (a lost or repeated point) changes them."""
+    prune = 4
+    print("pruned sort: identical points", flush=True)
+    same = np.ones((5000, 3), np.float32) * np.float32(0.25)
+    lab, cnt, _ = gpu_fit(apd, same, 0.0, 5000, flags=prune)
+    assert np.all(cnt == 5000) and np.all(lab == 0)
+    print("pruned sort: ascending and descending chains", flush=True)
+    chain = datagen.collinear_chain(100000, 0.5)
+    want_c = np.full(100000, 3, np.int32)
+    want_c[[0, -1]] = 2
+    for pts in (chain, np.ascontiguousarray(chain[::-1])):
+        lab, cnt, _ = gpu_fit(apd, pts, 0.5, 2, flags=prune)
+        assert np.array_equal(cnt, want_c) and np.all(lab == 0)
+    print("pruned sort: few distinct points, ragged sizes", flush=True)
+    rng = np.random.default_rng(11)
+    for n in (1023, 1025, 9000):
+        sites = datagen.uniform_points(40, 2, 12)
+        x = np.ascontiguousarray(sites[rng.integers(0, 40, n)])
+        want_l, want_c, _ = orc.fit(x, 0.02, 30)
+        lab, cnt, _ = gpu_fit(apd, x, 0.02, 30, flags=prune)
+        assert_same(lab, cnt, want_l, want_c, f"few sites n={n}")
+
+
 def test_edge_area_overflow_falls_back(apd, orc):
     x = datagen.gaussian_blobs(20000, 2, seed=3, n_blobs=4, sigma=0.05)
     want_l, want_c, _ = orc.fit(x, 0.02, 8)
