@@ -91,7 +91,8 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
                                            const float* __restrict__ srow,
                                            const float* __restrict__ ncol,
                                            const float* __restrict__ nexp,
-                                           float* rows_lds) {
+                                           float* rows_lds, unsigned* rowc,
+                                           int64_t n_real) {
   constexpr int S = row_stride(D);
   constexpr int SR = screen_stride(D);
   const int lane = lane_id();
@@ -112,9 +113,39 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
     for (int k = 0; k < D; ++k) asm volatile("" : "+v"(xc[p][k]));
     if (SCREEN) asm volatile("" : "+v"(ny[p]));
   }
-  unsigned lc[P];
+  // Narrow points (16 groups per lane), where most rows have a pair: the
+  // row's pairs become one pattern per lane (bit P-1-p: group p), taken
+  // from the signs of val - e2n, e2n the float just above eps2.  val <=
+  // eps2 exactly when val - e2n < 0 (a rounded difference has the sign of
+  // the exact one and is +0 only for equal operands; subnormals are
+  // kept), so a group costs a full-rate subtraction and a bit shift, where
+  // a compare and a carry-in add read a mask from scalar registers at half
+  // rate.  Padding columns (NaN, sign unspecified) are masked out; padding
+  // rows never get here (a NaN row has no candidate).  No float lies above
+  // +inf: with eps2 = +inf the pattern comes from ballots.  The row counts
+  // go through LDS (a byte per row and lane, summed every 64 rows) and the
+  // column counts through 8-bit counters, four to a register, moved into
+  // 16-bit counters, two to a register, every 64 rows (at most 64 and
+  // 4096 a counter).
+  constexpr bool SIGNS = !SCREEN && P >= 16;
+  constexpr int NLC = SIGNS ? 1 : P;
+  unsigned lc[NLC];
 #pragma unroll
-  for (int p = 0; p < P; ++p) lc[p] = 0;
+  for (int p = 0; p < NLC; ++p) lc[p] = 0;
+  unsigned lcw[SIGNS ? P / 2 : 1];  // half h of lcw[k]: pattern bit 2k + h
+  unsigned lcb[SIGNS ? P / 4 : 1];  // byte b of lcb[g]: pattern bit 4g + b
+  unsigned colvalid = 0;
+  bool signs = false;
+  float e2n = 0.f;
+  if constexpr (SIGNS) {
+#pragma unroll
+    for (int k = 0; k < P / 2; ++k) lcw[k] = 0u;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      colvalid = (colvalid << 1) | (colw + p * 64 + lane < n_real ? 1u : 0u);
+    signs = __float_as_uint(eps2) < 0x7f800000u;
+    e2n = __uint_as_float(__float_as_uint(eps2) + 1u);
+  }
 
   for (int rb = 0; rb < rows; rb += 64) {
     // pruned: skip 64 rows whose box is provably farther than eps from
@@ -157,6 +188,14 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
       far_rows = ballot(sg > eps2);
     }
     int rowv = 0;  // lane l: count of row rb+l over these columns
+    if constexpr (SIGNS) {
+      uint4* z = reinterpret_cast<uint4*>(rowc) + lane * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) z[k] = make_uint4(0u, 0u, 0u, 0u);
+      wave_lds_sync();
+#pragma unroll
+      for (int g = 0; g < P / 4; ++g) lcb[g] = 0u;
+    }
     if (SCREEN) {
       // the 64 rows' records (-2x, lo, hi) go to the wave's LDS area with
       // one coalesced load (lane l: row rb + l); each row is then read
@@ -243,129 +282,197 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 #pragma unroll
       for (int p = 1; p < P; ++p) vmin = __builtin_fminf(vmin, val[p]);
       unsigned acc = 0;
-      uint64_t m[P];
+      uint64_t m[SIGNS ? 1 : P];
       if (ballot(vmin <= thr)) {
-        if (SCREEN) {
-          uint64_t amb = 0;
+        if constexpr (SIGNS) {
+          unsigned pat = 0;
+          if (signs) {
 #pragma unroll
-          for (int p = 0; p < P; ++p) {
-            m[p] = ballot(val[p] <= lo);
-            amb |= ballot(val[p] <= thr) & ~m[p];
+            for (int p = 0; p < P; ++p)
+              pat = __builtin_amdgcn_alignbit(
+                  pat, __float_as_uint(val[p] - e2n), 31u);
+            pat &= colvalid;
+          } else {
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+              pat = shift_in_lane_bit(pat, ballot(val[p] <= eps2));
           }
-          if (amb) {
-            // some pair of this row lies inside the bound: decide the
-            // pairs of each group that holds one with the exact distance
-            // (or, given its norms, the exact hoisted-norm form); the
-            // other groups keep their screened masks
-            const const_float_ptr rp = (const_float_ptr)(pts + row * S);
-            float xr[D];
+          reinterpret_cast<unsigned char*>(rowc)[l * 64 + lane] =
+              (unsigned char)__builtin_popcount(pat);
+          if (!DIAG) {
+            // nibble g of the pattern spread to the bytes of a word
 #pragma unroll
-            for (int k = 0; k < D; ++k) xr[k] = rp[k];
-            const float tr = !PRUNED && nexp != nullptr
-                                 ? ((const_float_ptr)nexp)[row] : 0.f;
+            for (int g = 0; g < P / 4; ++g)
+              lcb[g] += (((pat >> (4 * g)) & 15u) * 0x204081u) & 0x01010101u;
+          }
+          if (EDGES) {
+            int lane_col = (int)(colw + lane);
+            asm volatile("" : "+v"(lane_col));
+            const int row_out = PRUNED ? ((const_int_ptr)perm)[row] : (int)row;
+            if (DIAG) {
+              // pairs with column > row only (each unordered pair once)
+              const int q = (int)(row - colw) - lane;
+              const int p0 = q < 0 ? 0 : (q >> 6) + 1;
+              pat = p0 >= P ? 0u : pat & ((2u << (P - 1 - p0)) - 1u);
+            }
+            stage_pairs(
+                pat,
+                [&](int b) {
+                  const int col = lane_col + (P - 1 - b) * 64;
+                  return make_uint2((unsigned)row_out,
+                                    (unsigned)(PRUNED ? perm[col] : col));
+                },
+                stage, fill, sink);
+          }
+        } else {
+          if (SCREEN) {
+            uint64_t amb = 0;
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-              if ((ballot(val[p] <= thr) & ~m[p]) == 0) continue;
-              if (!PRUNED && nexp != nullptr)
-                m[p] = ballot(expanded_d2<D>(xr, xc[p], tr,
-                                             nexp[colw + p * 64 + lane]) <= eps2);
-              else
-                m[p] = ballot(dist2<D>(xr, xc[p]) <= eps2);
+              m[p] = ballot(val[p] <= lo);
+              amb |= ballot(val[p] <= thr) & ~m[p];
             }
-          }
-        } else {
+            if (amb) {
+              // some pair of this row lies inside the bound: decide the
+              // pairs of each group that holds one with the exact distance
+              // (or, given its norms, the exact hoisted-norm form); the
+              // other groups keep their screened masks
+              const const_float_ptr rp = (const_float_ptr)(pts + row * S);
+              float xr[D];
 #pragma unroll
-          for (int p = 0; p < P; ++p) m[p] = ballot(val[p] <= eps2);
-        }
+              for (int k = 0; k < D; ++k) xr[k] = rp[k];
+              const float tr = !PRUNED && nexp != nullptr
+                                   ? ((const_float_ptr)nexp)[row] : 0.f;
 #pragma unroll
-        for (int p = 0; p < P; ++p) acc += (unsigned)__popcll(m[p]);
-        if (!DIAG && P < 16) {
-          // Off the diagonal with few groups per lane: only groups with a
-          // pair pay for the lane counter and the staging (one wave-uniform
-          // test each), and the group's mask is the exec mask of its
-          // stores.  One check makes room for the whole row (at most 64 P
-          // <= 512 pairs).  200k x 8: count 7.46 -> 7.32 ms; 262k x 64:
-          // 104.3 -> 99.3 ms (two registers fewer, five waves per SIMD).
-          if (EDGES && acc != 0 && fill + acc > (unsigned)kEdgeStage) {
-            flush_edges(stage, fill, sink);
-            fill = 0;
-          }
-          int lane_col = (int)(colw + lane);
-          asm volatile("" : "+v"(lane_col));
-          const int row_out =
-              PRUNED && EDGES ? ((const_int_ptr)perm)[row] : (int)row;
-#pragma unroll
-          for (int p = 0; p < P; ++p) {
-            if (m[p] == 0) continue;
-            lc[p] = add_lane_bit(lc[p], m[p]);
-            if (EDGES) {
-              if (__builtin_amdgcn_inverse_ballot_w64(m[p])) {
-                const int col = lane_col + p * 64;
-                stage[fill + bits_below(m[p])] = make_uint2(
-                    (unsigned)row_out, (unsigned)(PRUNED ? perm[col] : col));
+              for (int p = 0; p < P; ++p) {
+                if ((ballot(val[p] <= thr) & ~m[p]) == 0) continue;
+                if (!PRUNED && nexp != nullptr)
+                  m[p] = ballot(expanded_d2<D>(xr, xc[p], tr,
+                                               nexp[colw + p * 64 + lane]) <=
+                                eps2);
+                else
+                  m[p] = ballot(dist2<D>(xr, xc[p]) <= eps2);
               }
-              fill += (unsigned)__popcll(m[p]);
             }
-          }
-        } else {
+          } else {
 #pragma unroll
-          for (int p = 0; p < P; ++p)
-            if (!DIAG) lc[p] = add_lane_bit(lc[p], m[p]);
-          if (EDGES && acc != 0) {
+            for (int p = 0; p < P; ++p) m[p] = ballot(val[p] <= eps2);
+          }
+#pragma unroll
+          for (int p = 0; p < P; ++p) acc += (unsigned)__popcll(m[p]);
+          if (!DIAG && P < 16) {
+            // Off the diagonal with few groups per lane: only groups with a
+            // pair pay for the lane counter and the staging (one wave-uniform
+            // test each), and the group's mask is the exec mask of its
+            // stores.  One check makes room for the whole row (at most 64 P
+            // <= 512 pairs).  200k x 8: count 7.46 -> 7.32 ms; 262k x 64:
+            // 104.3 -> 99.3 ms (two registers fewer, five waves per SIMD).
+            if (EDGES && acc != 0 && fill + acc > (unsigned)kEdgeStage) {
+              flush_edges(stage, fill, sink);
+              fill = 0;
+            }
             int lane_col = (int)(colw + lane);
-            // recomputed here, on the rare path, instead of P live registers
             asm volatile("" : "+v"(lane_col));
             const int row_out =
-                PRUNED ? ((const_int_ptr)perm)[row] : (int)row;
-            if constexpr (P >= 16) {
-              // many groups per row (narrow points, dense rows): collect the
-              // lane's pairs of all groups (group p's bit at position P-1-p)
-              // and pack them with one prefix sum over the lanes
-              unsigned pat = 0;
+                PRUNED && EDGES ? ((const_int_ptr)perm)[row] : (int)row;
 #pragma unroll
-              for (int p = 0; p < P; ++p) pat = shift_in_lane_bit(pat, m[p]);
-              if (DIAG) {
-                // pairs with column > row only (each unordered pair once,
-                // never (i, i)): the lane's column of group p exceeds the
-                // row for p >= p0
-                const int q = (int)(row - colw) - lane;
-                const int p0 = q < 0 ? 0 : (q >> 6) + 1;
-                pat = p0 >= P ? 0u : pat & ((2u << (P - 1 - p0)) - 1u);
-              }
-              stage_pairs(
-                  pat,
-                  [&](int b) {
-                    const int col = lane_col + (P - 1 - b) * 64;
-                    return make_uint2((unsigned)row_out,
-                                      (unsigned)(PRUNED ? perm[col] : col));
-                  },
-                  stage, fill, sink);
-            } else {
-              // few groups on a diagonal tile: one ballot scan per group
-              // with a pair, at most 8 groups (512 pairs) per capacity check
-#pragma unroll
-              for (int g = 0; g < P; g += 8) {
-                constexpr int G = P < 8 ? P : 8;
-                unsigned want = 0;
-#pragma unroll
-                for (int p = g; p < g + G; ++p) want += (unsigned)__popcll(m[p]);
-                if (fill + want > (unsigned)kEdgeStage) {
-                  flush_edges(stage, fill, sink);
-                  fill = 0;
-                }
-#pragma unroll
-                for (int p = g; p < g + G; ++p) {
+            for (int p = 0; p < P; ++p) {
+              if (m[p] == 0) continue;
+              lc[p] = add_lane_bit(lc[p], m[p]);
+              if (EDGES) {
+                if (__builtin_amdgcn_inverse_ballot_w64(m[p])) {
                   const int col = lane_col + p * 64;
-                  stage_edges<DIAG>(m[p], row, colw + p * 64, row_out,
-                                    PRUNED ? perm[col] : col, stage, fill);
+                  stage[fill + bits_below(m[p])] = make_uint2(
+                      (unsigned)row_out, (unsigned)(PRUNED ? perm[col] : col));
+                }
+                fill += (unsigned)__popcll(m[p]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+              if (!DIAG) lc[p] = add_lane_bit(lc[p], m[p]);
+            if (EDGES && acc != 0) {
+              int lane_col = (int)(colw + lane);
+              // recomputed here, on the rare path, instead of P live registers
+              asm volatile("" : "+v"(lane_col));
+              const int row_out =
+                  PRUNED ? ((const_int_ptr)perm)[row] : (int)row;
+              if constexpr (P >= 16) {
+                // many groups per row (narrow points, dense rows): collect the
+                // lane's pairs of all groups (group p's bit at position P-1-p)
+                // and pack them with one prefix sum over the lanes
+                unsigned pat = 0;
+#pragma unroll
+                for (int p = 0; p < P; ++p) pat = shift_in_lane_bit(pat, m[p]);
+                if (DIAG) {
+                  // pairs with column > row only (each unordered pair once,
+                  // never (i, i)): the lane's column of group p exceeds the
+                  // row for p >= p0
+                  const int q = (int)(row - colw) - lane;
+                  const int p0 = q < 0 ? 0 : (q >> 6) + 1;
+                  pat = p0 >= P ? 0u : pat & ((2u << (P - 1 - p0)) - 1u);
+                }
+                stage_pairs(
+                    pat,
+                    [&](int b) {
+                      const int col = lane_col + (P - 1 - b) * 64;
+                      return make_uint2((unsigned)row_out,
+                                        (unsigned)(PRUNED ? perm[col] : col));
+                    },
+                    stage, fill, sink);
+              } else {
+                // few groups on a diagonal tile: one ballot scan per group
+                // with a pair, at most 8 groups (512 pairs) per capacity check
+#pragma unroll
+                for (int g = 0; g < P; g += 8) {
+                  constexpr int G = P < 8 ? P : 8;
+                  unsigned want = 0;
+#pragma unroll
+                  for (int p = g; p < g + G; ++p)
+                    want += (unsigned)__popcll(m[p]);
+                  if (fill + want > (unsigned)kEdgeStage) {
+                    flush_edges(stage, fill, sink);
+                    fill = 0;
+                  }
+#pragma unroll
+                  for (int p = g; p < g + G; ++p) {
+                    const int col = lane_col + p * 64;
+                    stage_edges<DIAG>(m[p], row, colw + p * 64, row_out,
+                                      PRUNED ? perm[col] : col, stage, fill);
+                  }
                 }
               }
             }
           }
+          // lane l of rowv holds row l's count; rows without a candidate
+          // leave it at the 0 it started from
+          rowv = write_lane(rowv, (int)acc, l);
         }
-        // lane l of rowv holds row l's count; rows without a candidate
-        // leave it at the 0 it started from
-        rowv = write_lane(rowv, (int)acc, l);
+      }
+    }
+    if constexpr (SIGNS) {
+      wave_lds_sync();
+      const uint4* rp = reinterpret_cast<const uint4*>(rowc) + lane * 4;
+      unsigned sum = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 w = rp[k];
+        sum = __builtin_amdgcn_sad_u8(w.x, 0u, sum);
+        sum = __builtin_amdgcn_sad_u8(w.y, 0u, sum);
+        sum = __builtin_amdgcn_sad_u8(w.z, 0u, sum);
+        sum = __builtin_amdgcn_sad_u8(w.w, 0u, sum);
+      }
+      rowv = (int)sum;
+      wave_lds_sync();
+      if (!DIAG) {
+        // bytes 0, 1 of lcb[g] to the halves of lcw[2g], bytes 2, 3 to
+        // those of lcw[2g+1] (selector 0x0c gives a zero byte)
+#pragma unroll
+        for (int g = 0; g < P / 4; ++g) {
+          lcw[2 * g] += __builtin_amdgcn_perm(0u, lcb[g], 0x0c010c00u);
+          lcw[2 * g + 1] += __builtin_amdgcn_perm(0u, lcb[g], 0x0c030c02u);
+        }
       }
     }
     if (rowv) {
@@ -375,11 +482,19 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
   }
   if (!DIAG) {
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      if (lc[p]) {
-        const int64_t c = colw + p * 64 + lane;
-        atomicAdd(count + (PRUNED ? perm[c] : c), lc[p]);
+    for (int p = 0; p < P; ++p) {
+      unsigned v;
+      if constexpr (SIGNS) {
+        const int q = P - 1 - p;  // the group's pattern bit
+        v = (lcw[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+      } else {
+        v = lc[p];
       }
+      if (v) {
+        const int64_t c = colw + p * 64 + lane;
+        atomicAdd(count + (PRUNED ? perm[c] : c), v);
+      }
+    }
   }
 }
 
@@ -401,9 +516,14 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, SCREEN), 8))) void k_count(
   constexpr int SR = screen_stride(D);
   __shared__ uint2 stage_all[EDGES ? 4 * kEdgeStage : 1];
   __shared__ __attribute__((aligned(16))) float rows_all[SCREEN ? 4 * 65 * SR : 1];
+  // narrow points: each wave's row counts, a byte per (row, lane)
+  constexpr bool ROWC = !SCREEN && P >= 16;
+  __shared__ __attribute__((aligned(16)))
+  unsigned rowc_all[ROWC ? 4 * 1024 : 1];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint2* stage = stage_all + (EDGES ? wave * kEdgeStage : 0);
   float* rows_lds = rows_all + (SCREEN ? wave * 65 * SR : 0);
+  unsigned* rowc = rowc_all + (ROWC ? wave * 1024 : 0);
   unsigned fill = 0;
   const EdgeSink sink{edges, cap, counter};
   // a non-finite input coordinate fails the fit: skip the pass
@@ -468,11 +588,11 @@ __attribute__((amdgpu_waves_per_eu(count_waves(D, SCREEN), 8))) void k_count(
     if (I == J)
       count_item<D, P, true, EDGES, PRUNED, SCREEN>(
           pts, row0, rows_eff, colw, eps2, count, stage, fill, sink, perm,
-          boxes64, boxes_w, box_thr, srow, ncol, nexp, rows_lds);
+          boxes64, boxes_w, box_thr, srow, ncol, nexp, rows_lds, rowc, n_real);
     else
       count_item<D, P, false, EDGES, PRUNED, SCREEN>(
           pts, row0, rows_eff, colw, eps2, count, stage, fill, sink, perm,
-          boxes64, boxes_w, box_thr, srow, ncol, nexp, rows_lds);
+          boxes64, boxes_w, box_thr, srow, ncol, nexp, rows_lds, rowc, n_real);
   }
   if (EDGES && fill) flush_edges(stage, fill, sink);
 }
