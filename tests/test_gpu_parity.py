@@ -174,6 +174,32 @@ def test_degenerate_inputs(apd, orc):
     assert_same(lab, cnt, want_l, want_c, "minpts 1")
 
 
+def test_narrow_radius_at_float_limits(apd, orc):
+    """2-d points (16 column groups per lane) with squared distances that
+    overflow to +inf.  eps = 1.8446744e19 squares to +inf (every pair is a
+    neighbour, the pattern comes from ballots); eps = 1.8446743e19 squares
+    to 3.4028233e38, the largest square of a float below +inf, so the
+    float just above it is finite and overflowed pairs are not
+    neighbours."""
+    rng = np.random.default_rng(21)
+    x = datagen.uniform_points(20000, 2, 22)   # 960 work items: P = 16
+    far = rng.integers(0, 20000, 60)
+    x[far, 0] = np.where(np.arange(60) % 2 == 0, np.float32(1.5e19),
+                         np.float32(-1.5e19))
+    for eps in (1.8446744e19, 1.8446743e19):
+        with np.errstate(over="ignore"):
+            e2 = np.float32(eps) * np.float32(eps)
+        print(f"narrow eps {eps} eps2 {e2}", flush=True)
+        want_l, want_c, _ = orc.fit(x, eps, 5)
+        for flags in (0, 4):
+            lab, cnt, _ = gpu_fit(apd, x, eps, 5, flags=flags)
+            assert_same(lab, cnt, want_l, want_c, f"eps {eps} flags {flags}")
+        if np.isinf(e2):
+            assert np.all(want_c == 20000)
+        else:
+            assert want_c.min() < 20000
+
+
 def test_pruned_key_sort_edge_cases(apd, orc):
     """The pruned mode's key sort on keys that are all equal, descending,
     or drawn from a few values: any permutation gives the same results,
