@@ -557,14 +557,32 @@ __global__ void k_tile_list(const float* __restrict__ boxes, int64_t nb, int S,
     const float* bj = boxes + J * 2 * S;
     bool keep = bi[0] <= bi[S] && bj[0] <= bj[S];  // both blocks hold points
     if (keep && I != J) {
+      // the gap of dimension k, squared, added in ascending k
       float s = 0.f;
-      for (int k = 0; k < S; ++k) {
-        const float loi = bi[k], hii = bi[S + k], loj = bj[k], hij = bj[S + k];
+      const auto add = [&s](int k, float loi, float hii, float loj, float hij) {
         float g = 0.f;
         if (loj > hii) g = loj - hii;
         else if (loi > hij) g = loi - hij;
         const float q = g * g;
         s = k == 0 ? q : s + q;
+      };
+      if (S % 4 == 0) {
+        // four dimensions a load, several loads in flight (the rows are
+        // 16-byte aligned: S is a multiple of 4 and the area 256-aligned)
+        const float4* li = reinterpret_cast<const float4*>(bi);
+        const float4* hi = reinterpret_cast<const float4*>(bi + S);
+        const float4* lj = reinterpret_cast<const float4*>(bj);
+        const float4* hj = reinterpret_cast<const float4*>(bj + S);
+#pragma unroll 4
+        for (int k4 = 0; k4 < S / 4; ++k4) {
+          const float4 a = li[k4], b = hi[k4], c = lj[k4], e = hj[k4];
+          add(4 * k4, a.x, b.x, c.x, e.x);
+          add(4 * k4 + 1, a.y, b.y, c.y, e.y);
+          add(4 * k4 + 2, a.z, b.z, c.z, e.z);
+          add(4 * k4 + 3, a.w, b.w, c.w, e.w);
+        }
+      } else {
+        for (int k = 0; k < S; ++k) add(k, bi[k], bi[S + k], bj[k], bj[S + k]);
       }
       keep = !(s > eps2);
     }
