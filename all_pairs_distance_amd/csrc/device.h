@@ -116,6 +116,17 @@ __device__ __forceinline__ unsigned add_lane_bit(unsigned cnt, uint64_t mask) {
   return cnt;
 }
 
+// add_lane_bit for a mask that a VALU instruction wrote at least two
+// instructions earlier: the wait states are already there, no padding
+// (the instruction-level tests check the distance in the built kernels).
+// 200k x 8 count 7.65 -> 7.58 ms with the shorter stage check beside it.
+__device__ __forceinline__ unsigned add_lane_bit_far(unsigned cnt,
+                                                     uint64_t mask) {
+  asm("v_addc_co_u32_e64 %0, vcc, %0, 0, %1"
+      : "+v"(cnt) : "s"(mask) : "vcc");
+  return cnt;
+}
+
 // 2*v + (bit `lane` of mask): shifts this lane's bit of a wave-uniform
 // mask into v, one VALU op (the same add-with-carry as add_lane_bit).
 __device__ __forceinline__ unsigned shift_in_lane_bit(unsigned v, uint64_t mask) {

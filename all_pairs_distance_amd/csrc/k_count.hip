@@ -367,7 +367,8 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
             // stores.  One check makes room for the whole row (at most 64 P
             // <= 512 pairs).  200k x 8: count 7.46 -> 7.32 ms; 262k x 64:
             // 104.3 -> 99.3 ms (two registers fewer, five waves per SIMD).
-            if (EDGES && acc != 0 && fill + acc > (unsigned)kEdgeStage) {
+            // (a candidate row has a pair, and fill never exceeds the stage)
+            if (EDGES && fill + acc > (unsigned)kEdgeStage) {
               flush_edges(stage, fill, sink);
               fill = 0;
             }
@@ -378,7 +379,9 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
 #pragma unroll
             for (int p = 0; p < P; ++p) {
               if (m[p] == 0) continue;
-              lc[p] = add_lane_bit(lc[p], m[p]);
+              // the masks were written by the compares above, many
+              // instructions back
+              lc[p] = add_lane_bit_far(lc[p], m[p]);
               if (EDGES) {
                 if (__builtin_amdgcn_inverse_ballot_w64(m[p])) {
                   const int col = lane_col + p * 64;
