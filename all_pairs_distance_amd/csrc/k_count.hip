@@ -17,7 +17,9 @@
 //   - the comparison becomes a 64-bit ballot: its popcount (scalar unit) is
 //     the row point's count over 64 columns, and each lane adds its own bit
 //     for the column point (the symmetric update of the Sammon-mapping
-//     page's "modified approach").
+//     page's "modified approach"); with 16 column points per lane (d <= 2)
+//     each lane builds its own pattern of the row's pairs from signs, and
+//     the row counts are summed through LDS.
 // Optionally every neighbour pair i<j is appended to an edge area so the
 // merge never evaluates a distance again.
 #include "count_common.h"
@@ -367,7 +369,8 @@ __device__ __forceinline__ void count_item(const float* __restrict__ pts,
             // stores.  One check makes room for the whole row (at most 64 P
             // <= 512 pairs).  200k x 8: count 7.46 -> 7.32 ms; 262k x 64:
             // 104.3 -> 99.3 ms (two registers fewer, five waves per SIMD).
-            // (a candidate row has a pair, and fill never exceeds the stage)
+            // (a row without a pair adds 0, and fill never exceeds the
+            // stage, so it never flushes here)
             if (EDGES && fill + acc > (unsigned)kEdgeStage) {
               flush_edges(stage, fill, sink);
               fill = 0;
