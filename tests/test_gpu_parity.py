@@ -144,6 +144,15 @@ def test_boundary_ties(apd, orc):
     x = np.array([[0.0], [1e-20], [3e-20]], np.float32)
     lab, cnt, _ = gpu_fit(apd, x, 0.0, 1)
     assert cnt.tolist() == [1, 1, 1] and lab.tolist() == [0, 1, 2]
+    # ties and near-ties among subnormal squares with 16 column points per
+    # lane (14,400 points: 640 work items), all tiles and pruned
+    lat = (datagen.integer_lattice(120, 2) * np.float32(1e-20)).astype(np.float32)
+    for eps in (1e-20, 1.5e-20):
+        want_l, want_c, _ = orc.fit(lat, eps, 5)
+        for flags in (0, 4):
+            lab, cnt, _ = gpu_fit(apd, lat, eps, 5, flags=flags)
+            assert_same(lab, cnt, want_l, want_c,
+                        f"subnormal lattice eps={eps} flags={flags}")
 
 
 def test_degenerate_inputs(apd, orc):
