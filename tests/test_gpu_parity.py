@@ -106,6 +106,22 @@ def test_every_dimension(apd, orc):
         assert_same(lab, cnt, want_l, want_c, f"d={d} pruned screen")
 
 
+def test_multi_column_kernels_every_width(apd, orc):
+    """Every width up to 16 at a size whose all-tiles pass runs the kernel
+    with P = 16, 8, 4 or 2 column points per lane (512 or more work items;
+    smaller sets take one point per lane), in the all-tiles, pruned and
+    screened modes."""
+    for d, n in ((1, 15000), (2, 15000), (3, 12000), (4, 12000), (6, 8000),
+                 (8, 8000), (12, 6000), (16, 6000)):
+        x = datagen.gaussian_blobs(n, d, seed=500 + d, n_blobs=5, sigma=0.03,
+                                   noise_frac=0.1)
+        eps = 0.02 * np.sqrt(d)
+        want_l, want_c, _ = orc.fit(x, eps, 6)
+        for flags in (0, 4, 8):
+            lab, cnt, _ = gpu_fit(apd, x, eps, 6, flags=flags)
+            assert_same(lab, cnt, want_l, want_c, f"d={d} n={n} flags={flags}")
+
+
 def test_pruning_skips_tiles_exactly(apd, orc):
     """Well separated blobs: most block pairs are pruned, results equal."""
     for d, n in ((1, 60000), (2, 50000), (3, 40000), (8, 20000)):
