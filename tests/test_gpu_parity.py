@@ -199,6 +199,47 @@ def test_degenerate_inputs(apd, orc):
     assert_same(lab, cnt, want_l, want_c, "minpts 1")
 
 
+def test_concurrent_fits_on_two_streams(apd, orc):
+    """Two host threads fit different sets at the same time, each on a
+    stream and a workspace of its own (calls keep no state between them),
+    three times each: every result equals its oracle."""
+    import threading
+    import torch
+    x1, e1, m1, _ = datagen.make_workload(2)
+    x2 = datagen.gaussian_blobs(30000, 3, seed=41, n_blobs=10, sigma=0.02,
+                                noise_frac=0.1)
+    sets = []
+    for x, eps, m in ((x1, e1, m1), (x2, 0.02, 6)):
+        want_l, want_c, _ = orc.fit(x, eps, m)
+        sets.append((torch.from_numpy(x).cuda(), eps, m, want_l, want_c,
+                     apd.Workspace(x.shape[0], x.shape[1], max_edges=1 << 26),
+                     torch.cuda.Stream()))
+    got = [[None] * 3 for _ in sets]
+    errors = []
+
+    def run(k):
+        xt, eps, m, _, _, ws, st = sets[k]
+        try:
+            with torch.cuda.stream(st):
+                for rep in range(3):
+                    lab, cnt = apd.fit(xt, eps, m, return_counts=True,
+                                       workspace=ws, stream=st)
+                    got[k][rep] = (lab.cpu().numpy(), cnt.cpu().numpy())
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for k, (_, _, _, want_l, want_c, _, _) in enumerate(sets):
+        for rep in range(3):
+            lab, cnt = got[k][rep]
+            assert_same(lab, cnt, want_l, want_c, f"set {k} call {rep}")
+
+
 def test_narrow_radius_at_float_limits(apd, orc):
     """2-d points (16 column groups per lane) with squared distances that
     overflow to +inf.  eps = 1.8446744e19 squares to +inf (every pair is a
