@@ -38,10 +38,12 @@ namespace dbk {
 // more registers: 5 waves, which its LDS (rows and pair stage, 28.5 KB per
 // work-group at width 8) allows anyway; asking for 6 left the allocator
 // at 4 (200k x 8 screened count 5.03 -> 4.80 ms with 5), and 7 or more
-// spill in the row loop.
+// spill in the row loop.  Widths up to 2 (16 column points per lane,
+// 117-124 VGPRs) take 4 waves: with 5 they spilled 18-25 registers, and
+// 4 ran 1% faster on 50k x 2 and 3-7% on sparser 2-d sets.
 constexpr int count_waves(int D, bool screen) {
   return screen ? (D <= 2 ? 4 : D <= 16 ? 5 : 1)
-                : (D <= 2 ? 5 : D <= 16 ? 8 : D >= 48 ? 6 : 1);
+                : (D <= 2 ? 4 : D <= 16 ? 8 : D >= 48 ? 6 : 1);
 }
 
 // Stage the pairs (row_out, col_out) of mask m, where row and col0 + lane
