@@ -57,8 +57,31 @@ constexpr int kSortPasses = 4;
 constexpr int kPcaSample = 1024;
 constexpr int kPcaIters = 30;
 
+// Sum over the wave by an xor butterfly (partners 32, 16, 8, 4, 2, 1, in
+// that order; both partners of a step form the same sum, so every lane
+// ends with the same total).  Only the step across the two halves goes
+// through the LDS crossbar; 16 is a swizzle within each half, and 8, 4, 2
+// and 1 are DPP moves within rows of 16 (4: two half-row moves under
+// bank masks).
+template <int CTRL>
+__device__ __forceinline__ float xor_lane_dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum_f(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v += __shfl_xor(v, 32);
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401f));
+  v += xor_lane_dpp<0x128>(v);  // row_ror:8 (lane ^ 8 within a row)
+  {
+    // lane ^ 4: banks 0 and 2 read 4 lanes up, banks 1 and 3 4 lanes down
+    int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xf, 0x5,
+                                        false);
+    t = __builtin_amdgcn_update_dpp(t, __float_as_int(v), 0x114, 0xf, 0xa,
+                                    false);
+    v += __int_as_float(t);
+  }
+  v += xor_lane_dpp<0x4e>(v);   // quad_perm 2,3,0,1 (lane ^ 2)
+  v += xor_lane_dpp<0xb1>(v);   // quad_perm 1,0,3,2 (lane ^ 1)
   return v;
 }
 
@@ -75,15 +98,26 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
   const int tid = threadIdx.x;
   const int64_t m = n < kPcaSample ? n : kPcaSample;
   const int64_t step = n / m;
+  // The sample in blocks of 64 points: thread t holds coordinate t % 64
+  // of points t / 64 + 4q (q < 16) of a block, and the next block's loads
+  // are issued before the current block is summed.
+  const int kk = tid & 63, r0 = tid >> 6;
+  float buf[16];
+  const auto load_block = [&](int64_t s0) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t smp = s0 + r0 + 4 * q;
+      buf[q] = (smp < m && kk < d) ? pts[smp * step * S + kk] : 0.f;
+    }
+  };
   // sample mean
   float msum = 0.f;
+  load_block(0);
   for (int64_t s0 = 0; s0 < m; s0 += 64) {
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int r = e >> 6, k = e & 63;
-      const int64_t smp = s0 + r;
-      tile[r][k] = (smp < m && k < d) ? pts[smp * step * S + k] : 0.f;
-    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) tile[r0 + 4 * q][kk] = buf[q];
     __syncthreads();
+    if (s0 + 64 < m) load_block(s0 + 64);
     if (tid < 64)
       for (int r = 0; r < 64; ++r) msum += tile[r][tid];
     __syncthreads();
@@ -95,13 +129,15 @@ __global__ __launch_bounds__(256) void k_pca(const float* __restrict__ pts,
   float c[4][4];
   for (int i = 0; i < 4; ++i)
     for (int j = 0; j < 4; ++j) c[i][j] = 0.f;
+  load_block(0);
   for (int64_t s0 = 0; s0 < m; s0 += 64) {
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int r = e >> 6, k = e & 63;
-      const int64_t smp = s0 + r;
-      tile[r][k] = (smp < m && k < d) ? pts[smp * step * S + k] - mean[k] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t smp = s0 + r0 + 4 * q;
+      tile[r0 + 4 * q][kk] = (smp < m && kk < d) ? buf[q] - mean[kk] : 0.f;
     }
     __syncthreads();
+    if (s0 + 64 < m) load_block(s0 + 64);
     for (int r = 0; r < 64; ++r) {
       float a[4], b[4];
       for (int i = 0; i < 4; ++i) {
